@@ -1,0 +1,377 @@
+"""Plain fp64 CPU oracle of the speculative-decoding verify sampler.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything under ``oracle/``.
+The product path (the HIP library and its binding) never imports it.
+
+The oracle follows the method's steps in order, one request and one row at a
+time, in float64 on the exact input values. A bf16 or fp32 logit converts to
+float64 without rounding. Citations name the page and the section:
+
+* Strata PR #3416 "[Engine] Preserve target probabilities in gated MTP",
+  section Approach. The retained measure mu = q * [q >= tau] is not
+  renormalised. A failed gate makes an explicit NULL row. An offered token D
+  is accepted with probability min(1, p(D)/mu(D)). Rejection and NULL both
+  draw from the normalised positive part of p - mu. A row with no attempted
+  proposal stays an ordinary target (bonus) sample.
+* regolith audit "rank-1 moce and step-aware speculative retention",
+  section schedule behavior. Equality passes the gate, and a failed gate ends
+  the contiguous prefix.
+* mlxcel PR #992, section What changed. The accept test compares a uniform
+  against p and q in the form u*q(t) <= p(t) and requires p(t) > 0, so that a
+  q that underflowed to zero cannot admit a token with p = 0. This oracle uses
+  the strict form u*mu(D) < p(D), which carries that p > 0 requirement. See
+  ``_accept``.
+* mlxcel PR #992, section Temperature 0. A greedy configuration turns p and q
+  into one-hot argmax indicators, so no randomness decides anything.
+* mlxcel PR #992, section Two metric corrections. A chain stops at its first
+  rejection, and the positions behind it are never tested.
+
+Readings where the pages leave a step open:
+
+* p = softmax(target/T) and q = softmax(draft/T), at the request's own
+  temperature T.
+* The residual draw is an exponential race: token = argmax_x w[x] / E[x],
+  with E[x] i.i.d. Exp(1) from Philox and ties going to the lower index. Its
+  law is w / sum(w). mlxcel PR #992 (section What changed) draws the same law
+  by Gumbel-max on log(w).
+* A residual with zero total mass falls back to a race over p.
+* draft_tokens[r] == -1, or any id outside [0, V), means "no proposal". Such a
+  row, and the last row of every request, is a bonus row: one race over p.
+* Temperature must be 0 or lie in [2**-14, 2**14]. tau must not be NaN.
+  Logits must be finite or -inf. A row that contains NaN or +inf, or holds
+  only -inf, is invalid, and so is its request. This is checked only on rows
+  the method actually evaluates. An invalid request emits nothing: its
+  accept length is -1 and all of its slots are -1.
+* row_offsets must be strictly increasing from 0 to R. Otherwise every output
+  is -1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import philox
+
+# Row verdicts (also the codes the GPU side reports in its row diagnostics).
+ACCEPT, REJECT, NULL, BONUS = 1, 2, 3, 4
+VERDICT_NAMES = {0: "untested", ACCEPT: "accept", REJECT: "reject", NULL: "null", BONUS: "bonus"}
+
+T_MIN = 2.0 ** -14
+T_MAX = 2.0 ** 14
+FLAG_EPS = 1e-6
+
+# Flag bits (decision boundaries within FLAG_EPS; see ``verify_request``).
+F_ACCEPT = 1      # F1: the accept uniform is near p(D)/mu(D)
+F_GATE = 2        # F2: q(D) is near tau
+F_RACE = 4        # F3: the two best race keys are near each other
+F_SUPPORT = 8     # F4: some q_x is near tau, or the residual mass is near 0, in a residual race
+
+
+# ---------------------------------------------------------------- decoding
+
+def decode_logits(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of bf16 (uint16 bit patterns) or fp32 logits."""
+    if dtype == "bf16":
+        bits = np.asarray(arr, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------- the method's steps
+
+def temperature_valid(T: float) -> bool:
+    return T == 0.0 or (T_MIN <= T <= T_MAX)
+
+
+def row_valid(logits: np.ndarray) -> bool:
+    """Finite or -inf everywhere, and at least one finite entry."""
+    if np.isnan(logits).any() or np.isposinf(logits).any():
+        return False
+    return bool(np.isfinite(logits).any())
+
+
+def argmax_lowest(x: np.ndarray) -> int:
+    """Index of the largest entry; ties go to the lowest index."""
+    return int(np.argmax(x))
+
+
+def softmax(logits: np.ndarray, T: float) -> np.ndarray:
+    """softmax(logits / T) in float64, max-subtracted. -inf entries get probability 0."""
+    z = logits / T
+    z = z - z.max()
+    e = np.exp(z)
+    return e / e.sum()
+
+
+def distribution(logits: np.ndarray, T: float) -> np.ndarray:
+    """p (target) or q (draft) at temperature T. T == 0 gives the one-hot argmax indicator."""
+    if T == 0.0:
+        out = np.zeros_like(logits)
+        out[argmax_lowest(logits)] = 1.0
+        return out
+    return softmax(logits, T)
+
+
+def retained_measure(q: np.ndarray, tau: float) -> np.ndarray:
+    """mu = q * [q >= tau], left unnormalised (Strata PR #3416, Approach)."""
+    return np.where(q >= tau, q, 0.0)
+
+
+def race(w: np.ndarray, E: np.ndarray) -> int:
+    """Exponential race: argmax_x w[x]/E[x], ties to the lower index. Law: w / sum(w)."""
+    return argmax_lowest(w / E)
+
+
+def _accept(u: float, mu_D: float, p_D: float) -> bool:
+    """Accept iff u*mu(D) < p(D). With u uniform on [0, 1) this has probability min(1, p/mu)."""
+    return u * mu_D < p_D
+
+
+# ---------------------------------------------------------------- one request
+
+@dataclass
+class RowRecord:
+    j: int
+    verdict: int
+    p_D: float = float("nan")
+    q_D: float = float("nan")
+    mu_D: float = float("nan")
+    u: float = float("nan")
+    resid_mass: float = float("nan")
+
+
+@dataclass
+class RequestResult:
+    tokens: list            # emitted tokens: k accepted drafts, then one residual/bonus token
+    accept_len: int         # k, or -1 for an invalid request
+    rows: list = field(default_factory=list)   # RowRecord per evaluated row
+    flags: int = 0          # OR of the F_* bits over evaluated rows
+
+
+def _top2_gap(keys: np.ndarray, cond: np.ndarray | None):
+    """Relative gap between the two largest keys and the larger of their sensitivity factors."""
+    if keys.size < 2:
+        return np.inf, 1.0
+    i2 = np.argpartition(-keys, 1)[:2]
+    a, b = (i2[0], i2[1]) if keys[i2[0]] >= keys[i2[1]] else (i2[1], i2[0])
+    k1, k2 = keys[a], keys[b]
+    if k1 <= 0.0:
+        return np.inf, 1.0
+    c = 1.0 if cond is None else max(cond[a], cond[b], 1.0)
+    return (k1 - k2) / k1, c
+
+
+def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau: float,
+                   seed: int, b: int, rule: str = "mu") -> RequestResult:
+    """Verify one request's window of rows.
+
+    ``tl``, ``dl`` are float64 [n, V] target and draft logits, and ``dt`` is
+    [n] draft tokens. Row n-1 is the bonus row. ``b`` is the request's index
+    in the batch, which keys its random stream.
+
+    ``rule`` selects the method ("mu") or a deliberately wrong rule that the
+    pages use as a negative control:
+
+    * "original": the biased gated verifier of Strata PR #3416, section
+      Problem and result. It accepts with min(1, p/q) using the unfiltered q,
+      draws from (p - q)+ on rejection, and turns a failed gate into a plain
+      target sample.
+    * "resample_p": mu acceptance, but a rejection resamples from p instead of
+      the residual. This is the naive mistake in mlxcel PR #992, section
+      The distributional argument.
+    * "argmax": argmax-against-argmax. D is accepted iff it is the target's
+      argmax, and a rejection emits that argmax (mlxcel PR #992, section The
+      acceptance ceiling).
+
+    Flags (method only, T > 0) mark requests whose result is decided within
+    FLAG_EPS of a boundary, where float32 arithmetic may legitimately decide
+    the other way:
+
+    * F1: an offered row with |u - p(D)/mu(D)| < eps.
+    * F2: tau > 0 and |q(D) - tau| < eps.
+    * F3: a race whose two best keys k1 >= k2 have (k1 - k2)/k1 < eps * c.
+      Here c = max(1, (p+mu)/r) over the two tokens of a residual race with
+      r = p - mu. That is the factor by which a relative error of eps in p
+      and mu moves the key r/E.
+    * F4: a residual race with some |q_x - tau| < eps (tau > 0), or a
+      residual mass below eps.
+    """
+    n, V = tl.shape
+    res = RequestResult(tokens=[], accept_len=-1)
+    if not temperature_valid(T) or np.isnan(tau):
+        return res
+    for j in range(n):
+        D = int(dt[j])
+        bonus = (j == n - 1) or not (0 <= D < V)
+        if not row_valid(tl[j]):
+            res.tokens = []
+            res.rows.append(RowRecord(j=j, verdict=0))
+            return res
+        p = distribution(tl[j], T)
+        if bonus:
+            E = philox.race_exponentials(seed, b, j, V)
+            tok = race(p, E)
+            if T > 0.0:
+                gap, _ = _top2_gap(p / E, None)
+                if gap < FLAG_EPS:
+                    res.flags |= F_RACE
+            res.tokens.append(tok)
+            res.rows.append(RowRecord(j=j, verdict=BONUS))
+            res.accept_len = len(res.tokens) - 1
+            return res
+        if not row_valid(dl[j]):
+            res.tokens = []
+            res.rows.append(RowRecord(j=j, verdict=0))
+            return res
+        q = distribution(dl[j], T)
+        rec = RowRecord(j=j, verdict=0, p_D=float(p[D]), q_D=float(q[D]))
+
+        if rule == "argmax":
+            am = argmax_lowest(p)
+            if D == am:
+                rec.verdict = ACCEPT
+                res.rows.append(rec)
+                res.tokens.append(D)
+                continue
+            rec.verdict = REJECT
+            res.rows.append(rec)
+            res.tokens.append(am)
+            res.accept_len = len(res.tokens) - 1
+            return res
+
+        mu = retained_measure(q, tau)
+        offered = q[D] >= tau
+        if rule == "mu" and T > 0.0 and tau > 0.0 and abs(q[D] - tau) < FLAG_EPS:
+            res.flags |= F_GATE
+        if offered:
+            mu_D = q[D] if rule == "original" else mu[D]
+            rec.mu_D = float(mu_D)
+            # At T == 0, p(D) is 0 or 1 and mu(D) <= 1, so u*mu(D) < p(D) has the
+            # same outcome for every u in [0, 1): no uniform is drawn.
+            u = philox.accept_uniform(seed, b, j) if T > 0.0 else 0.0
+            rec.u = u if T > 0.0 else float("nan")
+            if rule == "mu" and T > 0.0 and mu_D > 0.0 and abs(u - p[D] / mu_D) < FLAG_EPS:
+                res.flags |= F_ACCEPT
+            if _accept(u, mu_D, p[D]):
+                rec.verdict = ACCEPT
+                res.rows.append(rec)
+                res.tokens.append(D)
+                continue
+            rec.verdict = REJECT
+        else:
+            rec.verdict = NULL
+            rec.mu_D = 0.0
+
+        # Rejection or NULL: draw from the normalised positive part of p - mu.
+        if rule == "original":
+            w = np.maximum(p - q, 0.0) if offered else p
+        elif rule == "resample_p":
+            w = p
+        else:
+            w = np.maximum(p - mu, 0.0)
+        R = float(w.sum())
+        rec.resid_mass = R
+        E = philox.race_exponentials(seed, b, j, V)
+        if R > 0.0:
+            tok = race(w, E)
+        else:
+            tok = race(p, E)
+        if rule == "mu" and T > 0.0:
+            if R > 0.0:
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    cond = np.where(w > 0.0, (p + mu) / np.where(w > 0.0, w, 1.0), 1.0)
+                gap, c = _top2_gap(w / E, cond)
+            else:
+                gap, c = _top2_gap(p / E, None)
+            if gap < FLAG_EPS * c:
+                res.flags |= F_RACE
+            if R < FLAG_EPS or (tau > 0.0 and bool((np.abs(q - tau) < FLAG_EPS).any())):
+                res.flags |= F_SUPPORT
+        res.rows.append(rec)
+        res.tokens.append(tok)
+        res.accept_len = len(res.tokens) - 1
+        return res
+    raise AssertionError("unreachable: the last row is always a bonus row")
+
+
+# ---------------------------------------------------------------- a batch
+
+def row_offsets_valid(ro: np.ndarray, R: int) -> bool:
+    ro = np.asarray(ro, dtype=np.int64)
+    if ro.size < 1 or ro[0] != 0 or ro[-1] != R:
+        return False
+    return bool(np.all(np.diff(ro) > 0))
+
+
+@dataclass
+class BatchResult:
+    out_tokens: np.ndarray      # [R] int32
+    out_accept_len: np.ndarray  # [B] int32
+    flags: np.ndarray           # [B] int32, F_* bits
+    verdict: np.ndarray         # [R] int32 (0 = row not tested)
+    p_D: np.ndarray             # [R] float64 (nan where not defined)
+    q_D: np.ndarray
+    mu_D: np.ndarray
+    u: np.ndarray
+    resid_mass: np.ndarray      # [R] float64, set on residual rows only
+
+
+def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int,
+                 dtype: str, requests=None, rule: str = "mu") -> BatchResult:
+    """Verify every request of a batch (or only those listed in ``requests``).
+
+    ``target`` and ``draft`` are [R, V] arrays of bf16 bit patterns (uint16) or
+    fp32 values. The other arguments mirror the C-ABI entry point. Requests not
+    in ``requests`` keep -1 outputs.
+    """
+    target = np.asarray(target)
+    R, V = target.shape
+    ro = np.asarray(row_offsets, dtype=np.int64)
+    B = ro.size - 1
+    out_tokens = np.full(R, -1, dtype=np.int32)
+    out_len = np.full(B, -1, dtype=np.int32)
+    flags = np.zeros(B, dtype=np.int32)
+    verdict = np.zeros(R, dtype=np.int32)
+    nan = lambda: np.full(R, np.nan)  # noqa: E731
+    p_D, q_D, mu_D, u, rm = nan(), nan(), nan(), nan(), nan()
+    if not row_offsets_valid(ro, R):
+        return BatchResult(out_tokens, out_len, flags, verdict, p_D, q_D, mu_D, u, rm)
+    temperature = np.asarray(temperature, dtype=np.float32).astype(np.float64)
+    tau = np.asarray(tau, dtype=np.float32).astype(np.float64)
+    dt = np.asarray(draft_tokens, dtype=np.int64)
+    todo = range(B) if requests is None else requests
+    for b in todo:
+        lo, hi = int(ro[b]), int(ro[b + 1])
+        tl = decode_logits(target[lo:hi], dtype)
+        dl = decode_logits(np.asarray(draft)[lo:hi], dtype)
+        rr = verify_request(tl, dl, dt[lo:hi], float(temperature[b]), float(tau[b]), seed, b, rule)
+        flags[b] = rr.flags
+        for rec in rr.rows:
+            r = lo + rec.j
+            verdict[r] = rec.verdict
+            p_D[r], q_D[r], mu_D[r], u[r], rm[r] = rec.p_D, rec.q_D, rec.mu_D, rec.u, rec.resid_mass
+        if rr.accept_len < 0:
+            continue
+        out_len[b] = rr.accept_len
+        out_tokens[lo:lo + len(rr.tokens)] = rr.tokens
+    return BatchResult(out_tokens, out_len, flags, verdict, p_D, q_D, mu_D, u, rm)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def acceptance_probability(p: np.ndarray, mu: np.ndarray) -> float:
+    """P(accept) of one offered-or-NULL row with D ~ q: sum_x min(p(x), mu(x)).
+
+    Ungated (mu = q) this is the maximal-coupling ceiling 1 - TV(p, q)
+    (mlxcel PR #992, section The acceptance ceiling).
+    """
+    return float(np.minimum(p, mu).sum())
+
+
+def sum_prod(p: np.ndarray, q: np.ndarray) -> float:
+    """sum_x p(x) q(x): acceptance of the sampler-match rule (mlxcel PR #992, The acceptance ceiling)."""
+    return float((p * q).sum())

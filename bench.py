@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of the verify sampler on one MI355X.
+
+One step is one full verify call (both kernels) over one batch of synthetic
+logits already resident in HBM. The default workload is the gated batch B=64,
+T=4 (+1 bonus row), V=151936, bf16 logits. Four distinct input sets rotate,
+so that repeated steps read HBM, not the 256 MB Infinity Cache.
+
+It prints ONE JSON line on stdout with:
+* verified rows/s (value);
+* the whole step's algorithmic bytes per second;
+* a roofline entry for the dominant kernel (pass 1), timed with HIP events
+  recorded on the launch stream around each kernel;
+* the CPU oracle timed on a bounded sample of the same workload on this
+  host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified rows/sec + achieved HBM GB/s (% of peak), B=64 T=4 V=151936 bf16"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_traffic_gated_B64_T4_V151936_bf16.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "lossless_rejection_sampling_row_amd", "csrc", f)
+                  for f in ("sv_kernels.hip", "sv_device.h", "sv_plan.h")]
+DEFAULT_SETS = {1: 2, 2: 8, 3: 4, 4: 2, 5: 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def proposal_rows(w) -> int:
+    """Rows pass 1 streams: every row before a request's first no-proposal row and before its last row."""
+    ro, dt, V = w.row_offsets, w.draft_tokens, w.V
+    n = 0
+    for b in range(w.B):
+        lo, hi = int(ro[b]), int(ro[b + 1])
+        for r in range(lo, hi - 1):
+            if not (0 <= dt[r] < V):
+                break
+            n += 1
+    return n
+
+
+def pass2_bytes(w, accept_len: np.ndarray, esize: int) -> int:
+    """Bytes the method must read to draw each request's last token."""
+    ro, dt, V = w.row_offsets, w.draft_tokens, w.V
+    tot = 0
+    for b in range(w.B):
+        k = int(accept_len[b])
+        if k < 0:
+            continue
+        lo, hi = int(ro[b]), int(ro[b + 1])
+        r = lo + k
+        bonus = (r == hi - 1) or not (0 <= dt[r] < V)
+        greedy = w.temperature[b] == 0
+        if bonus:
+            tot += V * esize                    # race (or argmax) over p
+        elif not greedy:
+            tot += 2 * V * esize                # race over (p - mu)+
+    return tot
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the oracle as it stands on one process over whole batches of this workload."""
+    from oracle import verify as ov
+    rows = 0
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        ov.verify_batch(w.target, w.draft, w.draft_tokens, w.row_offsets, w.temperature, w.tau,
+                        calls, w.dtype)
+        rows += w.R
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full batches of the same workload (seeds 0..{calls - 1}), "
+                      f"{rows} rows in {el:.1f} s, one process (numpy, single-threaded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--sets", type=int, default=None, help="distinct input sets rotated through")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this verify "
+              f"path is measured on a single MI355X; requests shard across GPUs with no "
+              f"exchange, so more GPUs are not run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from lossless_rejection_sampling_row_amd import binding
+    from lossless_rejection_sampling_row_amd import workloads as wl
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nsets = args.sets or DEFAULT_SETS[args.config]
+    log(f"[bench] generating {nsets} input sets of {wl.CONFIG_NAMES[args.config]}")
+    sets = []
+    for i in range(nsets):
+        w = wl.config(args.config, rng_seed=wl.CONFIGS[args.config].rng_seed + 7919 * i)
+        esize = 2 if w.dtype == "bf16" else 4
+        if w.dtype == "bf16":
+            tgt = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev)
+            dft = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            tgt = torch.from_numpy(w.target).to(dev)
+            dft = torch.from_numpy(w.draft).to(dev)
+        g = dict(target=tgt, draft=dft,
+                 draft_tokens=torch.from_numpy(w.draft_tokens).to(dev),
+                 row_offsets=torch.from_numpy(w.row_offsets).to(dev),
+                 temperature=torch.from_numpy(w.temperature).to(dev),
+                 tau=torch.from_numpy(w.tau).to(dev))
+        sets.append((w, g))
+    w0 = sets[0][0]
+    B, R, V = w0.B, w0.R, w0.V
+    K, W = args.steps, args.warmup
+    ws = torch.zeros(binding.workspace_bytes(B, R, V, sets[0][1]["target"].dtype), dtype=torch.uint8, device=dev)
+    out_tok = torch.empty((K, R), dtype=torch.int32, device=dev)
+    out_len = torch.empty((K, B), dtype=torch.int32, device=dev)
+    scratch_tok = torch.empty(R, dtype=torch.int32, device=dev)
+    scratch_len = torch.empty(B, dtype=torch.int32, device=dev)
+    ev = binding.HipEvents(3 * K)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, timed):
+        w, g = sets[i % nsets]
+        kw = dict(workspace=ws, stream=stream)
+        if timed:
+            kw.update(out_tokens=out_tok[i], out_accept_len=out_len[i], events=ev.handles[3 * i:3 * i + 3])
+        else:
+            kw.update(out_tokens=scratch_tok, out_accept_len=scratch_len)
+        binding.verify_batch(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"],
+                             g["temperature"], g["tau"], 1_000_003 * i + 17, **kw)
+
+    log(f"[bench] warmup {W} steps")
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    p1_ms = np.array([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(K)])
+    p2_ms = np.array([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(K)])
+    lens = out_len.cpu().numpy()
+    ev.close()
+
+    esize = 2 if w0.dtype == "bf16" else 4
+    prop = [proposal_rows(w) for w, _ in sets]
+    p1_bytes = np.array([prop[i % nsets] * V * 2 * esize for i in range(K)], dtype=np.float64)
+    p2_bytes = np.array([pass2_bytes(sets[i % nsets][0], lens[i], esize) for i in range(K)], dtype=np.float64)
+    small = 16 * R + 8 * B
+    alg = p1_bytes + p2_bytes + small
+    ms_per_step = total_ms / K
+    rows_per_s = R * K / (total_ms / 1e3)
+    step_gbps = alg.sum() / (total_ms / 1e3) / 1e9
+    p1_gbps = p1_bytes.mean() / (p1_ms.mean() / 1e3) / 1e9
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step; pass1 {p1_ms.mean() * 1e3:.1f} us "
+        f"({p1_gbps:.0f} GB/s); pass2 {p2_ms.mean() * 1e3:.1f} us; step {step_gbps:.0f} GB/s")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and args.config == 3:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(p1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(p1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "pass1_kernel", "launch_us": round(float(p1_ms.mean()) * 1e3, 2),
+                "alg_bytes_per_launch": int(p1_bytes.mean())}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(w0, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.CONFIG_NAMES[args.config], "B": B, "rows": R, "V": V,
+                   "logits": w0.dtype, "input_sets": nsets},
+        "achieved_gbps": round(step_gbps, 1),
+        "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "pass2_us": round(float(p2_ms.mean()) * 1e3, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * sv_verify.h - C ABI of the MI355X speculative-decoding verify sampler.
+ *
+ * The operation is mu-gated lossless rejection sampling over a batch of
+ * speculative windows. Per request b with rows ro[b] .. ro[b+1]-1 (one row
+ * per drafted position, plus a final bonus row):
+ *
+ *  - p = softmax(target_logits[row] / T_b), q = softmax(draft_logits[row] / T_b).
+ *  - Retained measure mu = q * [q >= tau_b], not renormalised. A drafted
+ *    token D whose gate fails (q(D) < tau_b) gives an explicit NULL row.
+ *    (Strata PR #3416 "[Engine] Preserve target probabilities in gated
+ *    MTP", section Approach.)
+ *  - An offered D is accepted with probability min(1, p(D)/mu(D)). The test
+ *    used is u*mu(D) < p(D), with u a Philox uniform on [0,1) keyed by
+ *    (seed, b, row position). This is the strict form of the accept test in
+ *    mlxcel PR #992, section What changed.
+ *  - Rejection or NULL ends the request with one draw from the normalised
+ *    positive part of p - mu (Strata PR #3416, section Approach). The draw
+ *    is an exponential race over the vocabulary, ties going to the lower
+ *    token id. A residual with zero mass draws from p instead.
+ *  - A request whose drafted tokens are all accepted, or which reaches a row
+ *    with no proposal, ends with a bonus draw from p (the same section).
+ *  - Each request stops at its first rejection, NULL or bonus row. The rows
+ *    behind it are never tested (mlxcel PR #992, section Two metric
+ *    corrections; regolith audit, section schedule behavior).
+ *  - Temperature 0 is greedy: p and q are one-hot argmax indicators (lowest
+ *    index on ties), and no randomness is drawn (mlxcel PR #992, section
+ *    Temperature 0).
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers (HIP), owned by the caller. The
+ *    library never allocates or frees caller memory. It keeps no pointer
+ *    after the enqueued work completes.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t, NULL = legacy default
+ *    stream). The call returns without synchronising. Outputs are valid once
+ *    the stream has passed the call.
+ *  - Host-checkable problems return a non-zero sv_status before anything is
+ *    enqueued, and leave the outputs untouched.
+ *  - The same inputs and seed give bit-identical outputs.
+ */
+#ifndef SV_VERIFY_H
+#define SV_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_E_NULLPTR = 1,     /* a required pointer is NULL                           */
+  SV_E_SHAPE = 2,       /* B < 0, R < 0, V <= 0, R < B, or B == 0 with R > 0     */
+  SV_E_DTYPE = 3,       /* dtype is not SV_F32 or SV_BF16                        */
+  SV_E_WORKSPACE = 4,   /* workspace smaller than sv_workspace_bytes(shape)      */
+  SV_E_UNSUPPORTED = 5, /* sizes beyond what the kernels index (see below)       */
+  SV_E_HIP = 6          /* a HIP launch or event call failed                     */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+enum { SV_NO_PROPOSAL = -1 };
+
+/* Row verdicts reported in sv_row_diag.verdict. */
+enum {
+  SV_ROW_UNTESTED = 0, /* the method never reached this row                         */
+  SV_ROW_ACCEPT = 1,   /* offered and accepted                                      */
+  SV_ROW_REJECT = 2,   /* offered and rejected: residual draw                       */
+  SV_ROW_NULL = 3,     /* gate failed (q(D) < tau): residual draw                   */
+  SV_ROW_BONUS = 4     /* last row or no proposal: draw from p                      */
+};
+
+typedef struct sv_shape {
+  int32_t B;     /* requests                                                     */
+  int32_t R;     /* total rows = row_offsets[B]                                  */
+  int32_t V;     /* vocabulary size (row length)                                 */
+  int32_t dtype; /* sv_dtype of target_logits and draft_logits                   */
+} sv_shape;
+
+/* Per-row diagnostics (32 bytes). Rows the method did not reach, and rows of
+ * invalid requests, hold verdict SV_ROW_UNTESTED and NaN values. */
+typedef struct sv_row_diag {
+  float p_D;        /* p(D) of an offered/NULL row (fp32 copy of an fp64 value) */
+  float q_D;        /* q(D)                                                     */
+  float mu_D;       /* mu(D) = q(D) if offered, else 0                          */
+  float u;          /* accept uniform (NaN at temperature 0)                    */
+  float resid_mass; /* sum_x (p - mu)+ on the row that drew the residual        */
+  int32_t verdict;  /* SV_ROW_*                                                 */
+  int32_t pad0;
+  int32_t pad1;
+} sv_row_diag;
+
+/* Batch counters (optional output). `rows_tested` counts drafted positions
+ * that were tested, which is the right denominator for per-position
+ * acceptance (mlxcel PR #992, section Two metric corrections). */
+typedef struct sv_batch_stats {
+  int64_t requests;     /* valid requests                                     */
+  int64_t rows_tested;  /* proposal rows tested (accepted + rejected + null)  */
+  int64_t accepted;
+  int64_t rejected;
+  int64_t null_rows;
+  int64_t bonus;        /* requests that ended with a bonus draw              */
+  int64_t greedy;       /* valid requests at temperature 0                    */
+  int64_t invalid;      /* requests failed closed on the device               */
+} sv_batch_stats;
+
+/*
+ * sv_verify_batch - verify every request of a batch.
+ *
+ * target_logits  [R, V] row-major, dtype. Rows that the method may read:
+ *                every proposal row and the row that ends each request.
+ * draft_logits   [R, V] same layout. Only proposal rows are read.
+ * draft_tokens   [R] int32. Drafted token D in [0, V), drawn by the drafter
+ *                from q. -1 (or any id outside [0, V)) means no proposal:
+ *                that row is a bonus row. The value on a request's last row
+ *                is ignored (it is always the bonus row).
+ * row_offsets    [B+1] int32. row_offsets[0] = 0, strictly increasing,
+ *                row_offsets[B] = R. Request b owns rows
+ *                [row_offsets[b], row_offsets[b+1]).
+ * temperature    [B] fp32. 0 = greedy. Otherwise it must lie in
+ *                [2^-14, 2^14].
+ * tau            [B] fp32. Gate threshold: the draft is offered iff
+ *                q(D) >= tau. 0 = ungated (mu = q). Must not be NaN.
+ * seed           64-bit Philox key. Give every verify step its own seed.
+ * out_tokens     [R] int32 output. Slots row_offsets[b] ..
+ *                row_offsets[b] + accept_len[b] hold the emitted tokens: the
+ *                accepted drafts, then the residual or bonus token. The other
+ *                slots are -1.
+ * out_accept_len [B] int32 output. Number of accepted drafts k, or -1 when
+ *                request b failed closed.
+ * shape          sizes and dtype (see sv_shape).
+ * workspace      device scratch of at least sv_workspace_bytes(shape)
+ *                bytes. It must be ZERO-FILLED before its first use. Every
+ *                completed call leaves its counters at zero again, so a
+ *                workspace can be reused by later calls of any shape that
+ *                fits. Calls that run at the same time must not share a
+ *                workspace.
+ * hip_stream     hipStream_t to enqueue on.
+ *
+ * Errors. Host-checkable problems return before anything is enqueued:
+ * SV_E_NULLPTR, SV_E_SHAPE, SV_E_DTYPE, SV_E_WORKSPACE, SV_E_UNSUPPORTED
+ * (V > 2^28 or R > 2^26). B == 0 with R == 0 is an empty batch: SV_OK,
+ * nothing enqueued. A failed launch returns SV_E_HIP. Bad data found on the
+ * device fails closed:
+ *  - temperature outside {0} U [2^-14, 2^14] or NaN, tau NaN, or an
+ *    evaluated row whose logits contain NaN or +inf or are all -inf: that
+ *    request gets accept_len -1 and all of its slots -1;
+ *  - row_offsets that are not strictly increasing from 0 to R: every
+ *    accept_len and every slot of out_tokens is -1.
+ * Logits must be finite with magnitude at most 2^64, or -inf.
+ */
+sv_status sv_verify_batch(const void* target_logits, const void* draft_logits,
+                          const int32_t* draft_tokens, const int32_t* row_offsets,
+                          const float* temperature, const float* tau, uint64_t seed,
+                          int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * sv_verify_batch_diag - sv_verify_batch plus optional diagnostics.
+ *
+ * It does the same work, with the same arguments and results.
+ * out_row_diag   [R] sv_row_diag (device), or NULL.
+ * out_stats      one sv_batch_stats (device), or NULL. It is overwritten.
+ * hip_events     NULL, or three hipEvent_t created by the caller. They are
+ *                recorded on hip_stream before the first kernel, between
+ *                the two kernels, and after the second. Elapsed times between
+ *                them give each kernel's duration.
+ */
+sv_status sv_verify_batch_diag(const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_tokens, const int32_t* row_offsets,
+                               const float* temperature, const float* tau, uint64_t seed,
+                               int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
+                               void* workspace, size_t workspace_bytes, void* hip_stream,
+                               sv_row_diag* out_row_diag, sv_batch_stats* out_stats,
+                               void* const* hip_events);
+
+/* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
+size_t sv_workspace_bytes(sv_shape shape);
+
+/* Static, human-readable name of a status code. Host-only. */
+const char* sv_status_string(int status);
+
+/* SV_ABI_VERSION of the loaded library. Host-only. */
+int sv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_VERIFY_H */

@@ -1,0 +1,209 @@
+"""ctypes binding of ``libsv_verify.so`` (declared in ``include/sv_verify.h``).
+
+This layer only marshals arguments. It checks torch tensors against the C
+ABI's layout, passes their device pointers and the current HIP stream, and
+returns torch tensors. Every step of the verify path runs in the library's
+kernels. There is no fallback: if the library is missing, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_int, c_int32, c_size_t, c_uint64, c_void_p
+
+ABI_VERSION = 1
+SV_F32, SV_BF16 = 0, 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class SvError(RuntimeError):
+    """A non-zero sv_status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class SvShape(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("R", c_int32), ("V", c_int32), ("dtype", c_int32)]
+
+
+def library_path() -> str:
+    return os.environ.get("SV_LIBRARY", os.path.join(_PKG, "libsv_verify.so"))
+
+
+def load_library():
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m lossless_rejection_sampling_row_amd.build`")
+    lib = ctypes.CDLL(path)
+    common = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_uint64,
+              c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
+    lib.sv_verify_batch.argtypes = common
+    lib.sv_verify_batch.restype = c_int
+    lib.sv_verify_batch_diag.argtypes = common + [c_void_p, c_void_p, POINTER(c_void_p)]
+    lib.sv_verify_batch_diag.restype = c_int
+    lib.sv_workspace_bytes.argtypes = [SvShape]
+    lib.sv_workspace_bytes.restype = c_size_t
+    lib.sv_status_string.argtypes = [c_int]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_abi_version.argtypes = []
+    lib.sv_abi_version.restype = c_int
+    if lib.sv_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path}: ABI version {lib.sv_abi_version()} != {ABI_VERSION}")
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().sv_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise SvError(status, status_string(status))
+
+
+def dtype_code(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return SV_BF16
+    if dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {dtype}")
+
+
+def workspace_bytes(B: int, R: int, V: int, dtype_or_code) -> int:
+    code = dtype_or_code if isinstance(dtype_or_code, int) else dtype_code(dtype_or_code)
+    return int(load_library().sv_workspace_bytes(SvShape(B, R, V, code)))
+
+
+_WORKSPACES: dict = {}
+
+
+def _workspace(device, nbytes: int):
+    """A zero-filled workspace per device, grown on demand. The library leaves it zeroed."""
+    import torch
+    key = (device.type, device.index)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def _ptr(t):
+    return c_void_p(t.data_ptr())
+
+
+def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int, *,
+                 out_tokens=None, out_accept_len=None, workspace=None, row_diag=None, stats=None,
+                 events=None, stream=None):
+    """Verify a batch of speculative windows on the GPU.
+
+    target, draft : [R, V] bfloat16 or float32 (same dtype), row-major, on one GPU.
+    draft_tokens  : [R] int32 (-1 = no proposal).
+    row_offsets   : [B+1] int32.
+    temperature   : [B] float32 (0 = greedy).
+    tau           : [B] float32 gate thresholds.
+    seed          : 64-bit Philox key.
+    row_diag      : optional [R, 8] int32 tensor that receives sv_row_diag records.
+    stats         : optional [8] int64 tensor that receives sv_batch_stats.
+    events        : optional sequence of three raw hipEvent_t handles (ints).
+    stream        : optional torch stream (default: the current stream).
+
+    Returns (out_tokens [R] int32, out_accept_len [B] int32). Work is enqueued
+    and not synchronised.
+    """
+    import torch
+    lib = load_library()
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU")
+    if draft.dtype != target.dtype or draft.shape != target.shape:
+        raise ValueError("target and draft must have the same dtype and shape")
+    if target.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = int(target.shape[0]), int(target.shape[1])
+    B = int(row_offsets.numel()) - 1
+    for name, t, dt, n in (("draft_tokens", draft_tokens, torch.int32, R),
+                           ("row_offsets", row_offsets, torch.int32, B + 1),
+                           ("temperature", temperature, torch.float32, B),
+                           ("tau", tau, torch.float32, B)):
+        if t.dtype != dt or t.numel() != n or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {dt} [{n}] on {dev}")
+    if not (target.is_contiguous() and draft.is_contiguous()):
+        raise ValueError("logits must be contiguous")
+    code = dtype_code(target.dtype)
+    shape = SvShape(B, R, V, code)
+    if out_tokens is None:
+        out_tokens = torch.empty(R, dtype=torch.int32, device=dev)
+    if out_accept_len is None:
+        out_accept_len = torch.empty(max(B, 0), dtype=torch.int32, device=dev)
+    need = int(lib.sv_workspace_bytes(shape))
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    args = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets), _ptr(temperature),
+            _ptr(tau), c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(out_tokens),
+            _ptr(out_accept_len), shape, _ptr(workspace), c_size_t(workspace.numel()),
+            c_void_p(stream.cuda_stream)]
+    if row_diag is None and stats is None and events is None:
+        _check(lib.sv_verify_batch(*args))
+    else:
+        if row_diag is not None and (row_diag.dtype != torch.int32 or row_diag.numel() != 8 * R):
+            raise ValueError("row_diag must be an int32 tensor with 8*R elements")
+        if stats is not None and (stats.dtype != torch.int64 or stats.numel() != 8):
+            raise ValueError("stats must be an int64 tensor with 8 elements")
+        ev = None
+        if events is not None:
+            ev = (c_void_p * 3)(*[c_void_p(int(e)) for e in events])
+        _check(lib.sv_verify_batch_diag(*args, _ptr(row_diag) if row_diag is not None else None,
+                                        _ptr(stats) if stats is not None else None, ev))
+    return out_tokens, out_accept_len
+
+
+def split_row_diag(row_diag):
+    """View an [R, 8] int32 sv_row_diag tensor as (p_D, q_D, mu_D, u, resid_mass, verdict)."""
+    import torch
+    d = row_diag.view(-1, 8)
+    f = d[:, :5].contiguous().view(torch.float32)
+    return f[:, 0], f[:, 1], f[:, 2], f[:, 3], f[:, 4], d[:, 5]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime (for sv_verify_batch_diag's timing hooks)."""
+
+    def __init__(self, n: int = 3):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [POINTER(c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [POINTER(ctypes.c_float), c_void_p, c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [c_void_p]
+        self._hip.hipEventDestroy.argtypes = [c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        self._hip.hipEventSynchronize(c_void_p(self.handles[j]))
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), c_void_p(self.handles[i]),
+                                         c_void_p(self.handles[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(c_void_p(h))
+        self.handles = []

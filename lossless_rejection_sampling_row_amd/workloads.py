@@ -5,7 +5,7 @@ of the verify method's arithmetic: it draws logits, rounds them to the storage
 type, plays the drafter by drawing one draft token per proposal row, and lays
 out the batch. A drafter samples its token from its own distribution q, so
 the token here is drawn by Gumbel-max (argmax of draft/T plus Gumbel noise
-from numpy's PCG64). That is the producer's job. The verifier only reads the
+from numpy's PCG64, in fp32). That is the producer's job. The verifier only reads the
 token.
 
 The pages measure on real models that are not available here (Llama-3.1-8B /
@@ -80,8 +80,12 @@ class Workload:
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -97,11 +101,15 @@ def _as_f32(stored: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _draw_tokens(rng, draft_f32: np.ndarray, T: float) -> np.ndarray:
-    """The drafter's draw D ~ softmax(draft/T), by Gumbel-max; T == 0 takes the argmax."""
+    """The drafter's draw D ~ softmax(draft/T) by Gumbel-max (-log of a unit exponential is Gumbel).
+
+    T == 0 takes the argmax.
+    """
     if T == 0.0:
         return np.argmax(draft_f32, axis=-1)
-    g = rng.gumbel(size=draft_f32.shape).astype(np.float64)
-    return np.argmax(draft_f32.astype(np.float64) / T + g, axis=-1)
+    e = rng.standard_exponential(size=draft_f32.shape, dtype=np.float32)
+    np.maximum(e, np.float32(1e-30), out=e)   # an exact 0 would give an infinite Gumbel
+    return np.argmax(draft_f32 * np.float32(1.0 / T) - np.log(e), axis=-1)
 
 
 def generate(spec: Spec, row_chunk: int = 256) -> Workload:
@@ -151,7 +159,7 @@ def generate(spec: Spec, row_chunk: int = 256) -> Workload:
         n = r1 - r0
         t = rng.standard_normal(size=(n, V), dtype=np.float32) * np.float32(spec.sigma_t)
         if spec.n_spikes > 0:
-            idx = np.argpartition(rng.random(size=(n, V), dtype=np.float32), spec.n_spikes, axis=1)[:, :spec.n_spikes]
+            idx = np.stack([rng.choice(V, size=spec.n_spikes, replace=False) for _ in range(n)])
             np.put_along_axis(t, idx, np.take_along_axis(t, idx, axis=1)
                               + np.float32(spec.spike_sigmas * spec.sigma_t), axis=1)
         noise = rng.standard_normal(size=(n, V), dtype=np.float32)

@@ -1,0 +1,161 @@
+"""The C-ABI library on a machine without a GPU.
+
+* The library loads and exports every function ``include/sv_verify.h`` declares.
+* Host-side validation returns the documented status codes before anything
+  touches the GPU: null pointers, bad shapes, bad dtype, small workspace,
+  unsupported sizes, and the empty batch.
+* The host core (planning and validation) is built on its own with g++ under
+  AddressSanitizer and UndefinedBehaviorSanitizer and driven through the same
+  paths. Strata PR #3416 (section Validation) runs its CPU proposal tests
+  under ASAN/UBSAN in the same way.
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv_verify.h")
+CSRC = os.path.join(ROOT, "lossless_rejection_sampling_row_amd", "csrc")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from lossless_rejection_sampling_row_amd import binding
+    if not os.path.exists(binding.library_path()):
+        pytest.fail("libsv_verify.so is not built (run python -m lossless_rejection_sampling_row_amd.build)")
+    return binding.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) >= {"sv_verify_batch", "sv_verify_batch_diag", "sv_workspace_bytes",
+                          "sv_status_string", "sv_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert lib.sv_abi_version() == 1
+
+
+def _call(lib, B, R, V, dtype, ws_bytes=1 << 30, null=None, diag=False):
+    from lossless_rejection_sampling_row_amd.binding import SvShape
+    fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails or B == 0
+    ptrs = [fake] * 6
+    outs = [fake, fake]
+    ws = fake
+    if null is not None:
+        if null < 6:
+            ptrs[null] = None
+        elif null < 8:
+            outs[null - 6] = None
+        else:
+            ws = None
+    args = [*ptrs, ctypes.c_uint64(1), *outs, SvShape(B, R, V, dtype), ws, ctypes.c_size_t(ws_bytes),
+            None]
+    if diag:
+        return lib.sv_verify_batch_diag(*args, None, None, None)
+    return lib.sv_verify_batch(*args)
+
+
+@pytest.mark.parametrize("diag", [False, True])
+def test_validation_codes(lib, diag):
+    SV_OK, NULLPTR, SHAPE, DTYPE, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+    assert _call(lib, 0, 0, 5, 1, diag=diag) == SV_OK            # empty batch
+    assert _call(lib, 0, 3, 5, 1, diag=diag) == SHAPE
+    assert _call(lib, -1, 3, 5, 1, diag=diag) == SHAPE
+    assert _call(lib, 2, 1, 5, 1, diag=diag) == SHAPE            # R < B
+    assert _call(lib, 2, 4, 0, 1, diag=diag) == SHAPE
+    assert _call(lib, 2, 4, -3, 0, diag=diag) == SHAPE
+    assert _call(lib, 2, 4, 5, 2, diag=diag) == DTYPE
+    assert _call(lib, 2, 4, 5, -1, diag=diag) == DTYPE
+    assert _call(lib, 2, 4, (1 << 28) + 1, 1, diag=diag) == UNSUPPORTED
+    assert _call(lib, 2, (1 << 26) + 1, 5, 1, diag=diag) == UNSUPPORTED
+    for i in range(9):
+        assert _call(lib, 2, 4, 5, 1, null=i, diag=diag) == NULLPTR
+    need = lib.sv_workspace_bytes(__import__("lossless_rejection_sampling_row_amd.binding",
+                                              fromlist=["SvShape"]).SvShape(2, 4, 5, 1))
+    assert need > 0
+    assert _call(lib, 2, 4, 5, 1, ws_bytes=need - 1, diag=diag) == WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    from lossless_rejection_sampling_row_amd.binding import SvShape
+    a = lib.sv_workspace_bytes(SvShape(64, 320, 151936, 1))
+    b = lib.sv_workspace_bytes(SvShape(64, 320, 151936, 0))
+    assert a > 0 and b > 0 and a % 256 == 0
+    assert lib.sv_workspace_bytes(SvShape(1, 0, 5, 1)) == 0     # invalid shape -> 0
+    assert lib.sv_workspace_bytes(SvShape(1, 1, 5, 9)) == 0
+    for code in range(7):
+        assert lib.sv_status_string(code).startswith(b"SV_")
+    assert lib.sv_status_string(99) == b"unknown sv_status"
+
+
+_DRIVER = r"""
+#include "sv_plan.h"
+#include <cstdio>
+#include <cstdlib>
+using namespace sv;
+static int fails = 0;
+#define CHECK(c) do { if (!(c)) { std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #c); ++fails; } } while (0)
+int main() {
+  Plan p;
+  int32_t dummy[4];
+  const void* v = dummy;
+  CHECK(make_plan(sv_shape{64, 320, 151936, SV_BF16}, &p) == SV_OK);
+  CHECK(p.s1 == 10 && p.s2 == 38 && p.total % 256 == 0 && p.off_ticket2 < p.total);
+  CHECK(make_plan(sv_shape{1, 1, 1, SV_F32}, &p) == SV_OK && p.s1 == 1 && p.s2 == 1);
+  CHECK(make_plan(sv_shape{0, 0, 7, SV_F32}, &p) == SV_OK);
+  CHECK(make_plan(sv_shape{3, 2, 7, SV_F32}, &p) == SV_E_SHAPE);
+  CHECK(make_plan(sv_shape{3, 4, 7, 5}, &p) == SV_E_DTYPE);
+  CHECK(make_plan(sv_shape{3, 4, 1 << 29, SV_F32}, &p) == SV_E_UNSUPPORTED);
+  CHECK(make_plan(sv_shape{2147483647, 2147483647, 1 << 28, SV_BF16}, &p) == SV_E_UNSUPPORTED);
+  for (int B = 1; B < 300; B += 37)
+    for (int V = 1; V < 300000; V = V * 3 + 1) {
+      CHECK(make_plan(sv_shape{B, 5 * B, V, SV_BF16}, &p) == SV_OK);
+      CHECK(sv_workspace_bytes(sv_shape{B, 5 * B, V, SV_BF16}) == p.total);
+      CHECK((long long)p.s1 * 256 * p.ept1 >= V && (long long)(p.s1 - 1) * 256 * p.ept1 < V);
+    }
+  const sv_shape ok{2, 4, 5, SV_F32};
+  CHECK(check_call(ok, v, v, dummy, dummy, (const float*)v, (const float*)v, dummy, dummy, v, 1 << 20, &p) == SV_OK);
+  CHECK(check_call(ok, nullptr, v, dummy, dummy, (const float*)v, (const float*)v, dummy, dummy, v, 1 << 20, &p) == SV_E_NULLPTR);
+  CHECK(check_call(ok, v, v, dummy, dummy, (const float*)v, (const float*)v, dummy, dummy, v, 8, &p) == SV_E_WORKSPACE);
+  CHECK(check_call(sv_shape{0, 0, 5, SV_F32}, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, &p) == SV_OK);
+  for (int s = -2; s < 10; ++s) CHECK(sv_status_string(s) != nullptr);
+  CHECK(sv_abi_version() == SV_ABI_VERSION);
+  std::printf("%s\n", fails ? "FAILED" : "OK");
+  return fails ? 1 : 0;
+}
+"""
+
+
+def test_host_core_under_sanitizers():
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    d = tempfile.mkdtemp(prefix="sv_core_asan_")
+    try:
+        drv = os.path.join(d, "driver.cpp")
+        exe = os.path.join(d, "driver")
+        with open(drv, "w") as f:
+            f.write(_DRIVER)
+        subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all", "-I", CSRC, drv, os.path.join(CSRC, "sv_core.cpp"),
+                        "-o", exe], check=True)
+        res = subprocess.run([exe], capture_output=True, text=True)
+        assert res.returncode == 0 and "OK" in res.stdout, res.stdout + res.stderr
+        # release build with asserts compiled out: the checks above are not asserts, they still run
+        subprocess.run([gxx, "-std=c++17", "-O2", "-DNDEBUG", "-I", CSRC, drv,
+                        os.path.join(CSRC, "sv_core.cpp"), "-o", exe], check=True)
+        res = subprocess.run([exe], capture_output=True, text=True)
+        assert res.returncode == 0 and "OK" in res.stdout, res.stdout + res.stderr
+    finally:
+        shutil.rmtree(d, ignore_errors=True)

@@ -133,11 +133,14 @@ typedef struct sv_batch_stats {
  *                request b failed closed.
  * shape          sizes and dtype (see sv_shape).
  * workspace      device scratch of at least sv_workspace_bytes(shape)
- *                bytes. It must be ZERO-FILLED before its first use. Every
- *                completed call leaves its counters at zero again, so a
- *                workspace can be reused by later calls of any shape that
- *                fits. Calls that run at the same time must not share a
- *                workspace.
+ *                bytes. Its contents need no preparation. The library keeps,
+ *                per device and workspace address, the counter layout of the
+ *                last call. When it sees a new address or a changed layout,
+ *                it clears the counters with a small kernel before the call.
+ *                Every completed call leaves them at zero again. So between
+ *                two calls that pass the same address with the same shape,
+ *                nothing else may write to the workspace. Calls that run at
+ *                the same time must not share a workspace.
  * hip_stream     hipStream_t to enqueue on.
  *
  * Errors. Host-checkable problems return before anything is enqueued:

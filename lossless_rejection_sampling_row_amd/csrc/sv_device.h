@@ -234,4 +234,84 @@ __device__ __forceinline__ void wave_top2(Top2& t) {
   }
 }
 
+
+// ------------------------------------------------------------------ hand-off between workgroups
+// A record that one wave writes and another wave (maybe on another XCD) reads in the same
+// kernel moves with agent-scope atomic loads and stores. Those are coherent across the
+// per-XCD L2 caches by themselves, so no cache write-back fence is needed. The writer waits
+// for its stores to complete before it takes the ticket, so the wave that draws the last
+// ticket reads complete records.
+
+__device__ __forceinline__ void store_word(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_word(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void publish(P1Part* dst, const P1Part& v) {
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  store_word(d + 0, __float_as_uint(v.m_t));
+  store_word(d + 1, __float_as_uint(v.s_t));
+  store_word(d + 2, __float_as_uint(v.m_d));
+  store_word(d + 3, __float_as_uint(v.s_d));
+  store_word(d + 4, (uint32_t)v.am_t);
+  store_word(d + 5, (uint32_t)v.am_d);
+  store_word(d + 6, (uint32_t)v.bad);
+  store_word(d + 7, (uint32_t)v.pad);
+}
+
+__device__ __forceinline__ P1Part read_p1(const P1Part* src) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+  P1Part v;
+  v.m_t = __uint_as_float(load_word(s + 0));
+  v.s_t = __uint_as_float(load_word(s + 1));
+  v.m_d = __uint_as_float(load_word(s + 2));
+  v.s_d = __uint_as_float(load_word(s + 3));
+  v.am_t = (int32_t)load_word(s + 4);
+  v.am_d = (int32_t)load_word(s + 5);
+  v.bad = (int32_t)load_word(s + 6);
+  v.pad = 0;
+  return v;
+}
+
+__device__ __forceinline__ void publish(P2Part* dst, const P2Part& v) {
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  store_word(d + 0, __float_as_uint(v.k1));
+  store_word(d + 1, __float_as_uint(v.k2));
+  store_word(d + 2, (uint32_t)v.i1);
+  store_word(d + 3, (uint32_t)v.i2);
+  store_word(d + 4, __float_as_uint(v.rsum));
+  store_word(d + 5, __float_as_uint(v.mref));
+  store_word(d + 6, (uint32_t)v.bad);
+  store_word(d + 7, (uint32_t)v.gidx);
+}
+
+__device__ __forceinline__ P2Part read_p2(const P2Part* src) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+  P2Part v;
+  v.k1 = __uint_as_float(load_word(s + 0));
+  v.k2 = __uint_as_float(load_word(s + 1));
+  v.i1 = (int32_t)load_word(s + 2);
+  v.i2 = (int32_t)load_word(s + 3);
+  v.rsum = __uint_as_float(load_word(s + 4));
+  v.mref = __uint_as_float(load_word(s + 5));
+  v.bad = (int32_t)load_word(s + 6);
+  v.gidx = (int32_t)load_word(s + 7);
+  return v;
+}
+
+// Arrive at a counter shared by `total` waves. Returns true in the wave that arrives last.
+// The counter wraps back to zero on the last arrival, ready for the next call.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, int lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's published records have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t old = 0;
+  if (lane == 0) old = atomicInc(counter, total - 1);
+  old = __shfl(old, 0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return old == total - 1;
+}
+
 }  // namespace sv

@@ -26,6 +26,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sv_device.h"
 #include "sv_plan.h"
 
@@ -211,7 +213,7 @@ __device__ void finalize_row(const Inputs& in, const Work& w, const Outputs& out
   float mt = -INFINITY, md = -INFINITY;
   int bad = 0;
   for (int i = lane; i < np; i += kWave) {
-    const P1Part q = pp[i];
+    const P1Part q = read_p1(pp + i);
     mt = fmaxf(mt, q.m_t);
     md = fmaxf(md, q.m_d);
     bad |= q.bad;
@@ -223,7 +225,7 @@ __device__ void finalize_row(const Inputs& in, const Work& w, const Outputs& out
   double st = 0.0, sd = 0.0;
   const float mct = ref_of(mt, c), mcd = ref_of(md, c);
   for (int i = lane; i < np; i += kWave) {
-    const P1Part q = pp[i];
+    const P1Part q = read_p1(pp + i);
     if (q.m_t == mt && q.am_t >= 0) it = min(it, q.am_t);
     if (q.m_d == md && q.am_d >= 0) id = min(id, q.am_d);
     if (!greedy) {
@@ -350,17 +352,10 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(Inputs in, Work w, Output
     pp.am_d = d.am;
     pp.bad = a.bad | d.bad;
     pp.pad = 0;
-    w.part1[((int64_t)r * in.s1 + chunk) * kWavesPerBlock + wave] = pp;
+    publish(&w.part1[((int64_t)r * in.s1 + chunk) * kWavesPerBlock + wave], pp);
   }
-  // The last wave of the row merges. Release our partial, take a ticket,
-  // and acquire everyone else's partials if we are last.
-  __threadfence();
-  const uint32_t total = (uint32_t)in.s1 * kWavesPerBlock;
-  uint32_t old = 0;
-  if (lane == 0) old = atomicInc(&w.ticket1[r], total - 1);  // wraps to 0 for the next call
-  old = __shfl(old, 0);
-  if (old != total - 1) return;
-  __threadfence();
+  // The last wave of the row merges every wave's partial.
+  if (!arrive_last(&w.ticket1[r], (uint32_t)in.s1 * kWavesPerBlock, lane)) return;
   finalize_row(in, w, out, r, cls, lane);
 }
 
@@ -710,13 +705,8 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   }
 
   const int np2 = in.s2 * kWavesPerBlock;
-  if (lane == 0) w.part2[(int64_t)b * np2 + (int64_t)chunk * kWavesPerBlock + wave] = part;
-  __threadfence();
-  uint32_t old = 0;
-  if (lane == 0) old = atomicInc(&w.ticket2[b], (uint32_t)np2 - 1);
-  old = __shfl(old, 0);
-  if (old != (uint32_t)np2 - 1) return;
-  __threadfence();
+  if (lane == 0) publish(&w.part2[(int64_t)b * np2 + (int64_t)chunk * kWavesPerBlock + wave], part);
+  if (!arrive_last(&w.ticket2[b], (uint32_t)np2, lane)) return;
 
   // ---- the request's last wave: merge the partials and emit
   const P2Part* pp = w.part2 + (int64_t)b * np2;
@@ -728,7 +718,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     double R = 0.0, bk = -1.0;
     int bi = INT32_MAX;
     for (int i = lane; i < np2; i += kWave) {
-      const P2Part c2 = pp[i];
+      const P2Part c2 = read_p2(pp + i);
       R += (double)c2.rsum;
       if (c2.i1 >= 0) {
         const double k = residual_key64(in, rr, q, b, c2.i1);
@@ -756,8 +746,9 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     float M = -INFINITY;
     int bad = 0;
     for (int i = lane; i < np2; i += kWave) {
-      M = fmaxf(M, pp[i].mref);
-      bad |= pp[i].bad;
+      const P2Part c2 = read_p2(pp + i);
+      M = fmaxf(M, c2.mref);
+      bad |= c2.bad;
     }
     M = wave_max(M);
     bad = wave_or(bad);
@@ -766,7 +757,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       double bk = -1.0;
       int bi = INT32_MAX;
       for (int i = lane; i < np2; i += kWave) {
-        const P2Part c2 = pp[i];
+        const P2Part c2 = read_p2(pp + i);
         if (q.kind == kGreedyBonus) {
           if (c2.mref == M && c2.gidx >= 0 && c2.gidx < bi) bi = c2.gidx;
         } else {
@@ -789,6 +780,55 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 }
 
 // ====================================================================== launch
+
+// Zero the two ticket arrays. Both tickets wrap back to zero when a call
+// completes, so this runs only when a workspace is first seen or its layout
+// changes (see counters_ready).
+__global__ __launch_bounds__(kBlock) void clear_counters_kernel(uint32_t* t1, int64_t n1, uint32_t* t2,
+                                                               int64_t n2) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n1; i += stride) t1[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n2; i += stride) t2[i] = 0u;
+}
+
+// Per (device, workspace address): the counter layout of the last call enqueued on it.
+struct LayoutSeen {
+  int device;
+  const void* ws;
+  size_t off_ticket1, off_ticket2;
+  int32_t R, B;
+};
+
+static std::mutex g_layout_mu;
+static LayoutSeen g_layout[64];
+static int g_layout_n = 0;
+
+// Make sure the workspace's ticket arrays hold zeros before pass 1 runs: clear them when
+// this (device, workspace) pair was not seen with this counter layout by the previous call.
+static hipError_t counters_ready(const Plan& p, char* ws, hipStream_t stream) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_layout_mu);
+  int slot = -1;
+  for (int i = 0; i < g_layout_n; ++i)
+    if (g_layout[i].device == dev && g_layout[i].ws == ws) slot = i;
+  if (slot >= 0 && g_layout[slot].off_ticket1 == p.off_ticket1 && g_layout[slot].off_ticket2 == p.off_ticket2 &&
+      g_layout[slot].R == p.R && g_layout[slot].B == p.B)
+    return hipSuccess;
+  const int64_t n = p.R > p.B ? p.R : p.B;
+  const unsigned grid = (unsigned)((n + kBlock - 1) / kBlock < 1024 ? (n + kBlock - 1) / kBlock : 1024);
+  hipLaunchKernelGGL(clear_counters_kernel, dim3(grid), dim3(kBlock), 0, stream,
+                     reinterpret_cast<uint32_t*>(ws + p.off_ticket1), (int64_t)p.R,
+                     reinterpret_cast<uint32_t*>(ws + p.off_ticket2), (int64_t)p.B);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (slot < 0) {
+    slot = g_layout_n < 64 ? g_layout_n++ : (int)(reinterpret_cast<uintptr_t>(ws) / 256 % 64);
+  }
+  g_layout[slot] = LayoutSeen{dev, ws, p.off_ticket1, p.off_ticket2, p.R, p.B};
+  return hipSuccess;
+}
+
 
 // Logits each lane holds per array: 128 bytes in pass 1, 32 bytes in pass 2.
 template <typename E> struct Ept;
@@ -835,7 +875,8 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
   const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 &&
                        (reinterpret_cast<uintptr_t>(target) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(draft) % 16) == 0;
-  hipError_t err;
+  hipError_t err = counters_ready(p, ws, stream);
+  if (err != hipSuccess) return SV_E_HIP;
   if (p.dtype == SV_BF16) {
     err = aligned ? launch_pair<uint16_t, 8>(p, in, w, out, stream, ev)
                   : launch_pair<uint16_t, 1>(p, in, w, out, stream, ev);

@@ -30,13 +30,15 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   q.V = s.V;
   q.dtype = s.dtype;
   q.esize = s.dtype == SV_BF16 ? 2 : 4;
-  // Each lane of pass 1 holds 128 bytes of target and 128 bytes of draft
-  // logits in registers (eight 16-byte loads per array); pass 2 holds a
-  // quarter of that per array.
-  q.ept1 = s.dtype == SV_BF16 ? 64 : 32;
-  q.ept2 = s.dtype == SV_BF16 ? 16 : 8;
-  q.s1 = (int32_t)ceil_div(s.V, (int64_t)kBlock * q.ept1);
-  q.s2 = (int32_t)ceil_div(s.V, (int64_t)kBlock * q.ept2);
+  // Long-lived waves: each one streams a contiguous span of a row. Pass 1 aims
+  // at about 3072 waves (3 per SIMD on 256 CUs) so that one round of waves
+  // covers the rows; pass 2 at about 4096. A row is never split into spans
+  // shorter than 8192 logits.
+  const int64_t max_split = s.V / 8192 > 1 ? s.V / 8192 : 1;
+  const int64_t want1 = s.R > 0 ? ceil_div(768, s.R) : 1;
+  const int64_t want2 = s.B > 0 ? ceil_div(1024, s.B) : 1;
+  q.s1 = (int32_t)(want1 < max_split ? want1 : max_split);
+  q.s2 = (int32_t)(want2 < max_split ? want2 : max_split);
   if ((int64_t)q.R * q.s1 > INT32_MAX || (int64_t)q.B * q.s2 > INT32_MAX) return SV_E_UNSUPPORTED;
   size_t off = 0;
   q.off_hdr = off;
@@ -45,10 +47,14 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   off += (size_t)q.R * q.s1 * kWavesPerBlock * sizeof(P1Part);
   q.off_rec = off = align_up(off, 256);
   off += (size_t)q.R * sizeof(RowRec);
-  q.off_ticket1 = off = align_up(off, 256);
-  off += (size_t)q.R * sizeof(uint32_t);
+  q.off_desc = off = align_up(off, 256);
+  off += (size_t)q.B * sizeof(ReqDesc);
   q.off_part2 = off = align_up(off, 256);
   off += (size_t)q.B * q.s2 * kWavesPerBlock * sizeof(P2Part);
+  q.off_ticket_row = off = align_up(off, 256);
+  off += (size_t)q.R * sizeof(uint32_t);
+  q.off_ticket_req = off = align_up(off, 256);
+  off += (size_t)q.B * sizeof(uint32_t);
   q.off_ticket2 = off = align_up(off, 256);
   off += (size_t)q.B * sizeof(uint32_t);
   q.total = align_up(off, 256);

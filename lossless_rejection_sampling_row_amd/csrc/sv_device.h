@@ -110,8 +110,22 @@ struct Chunk<uint16_t, 8> {
   uint4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
   __device__ __forceinline__ void fill_neg_inf() { v = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
+  __device__ __forceinline__ void select_if(bool c, const Chunk& o) {
+    v.x = c ? o.v.x : v.x;
+    v.y = c ? o.v.y : v.y;
+    v.z = c ? o.v.z : v.z;
+    v.w = c ? o.v.w : v.w;
+  }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t d = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? bf16_hi(d) : bf16_lo(d);
+  }
+  // Runtime element index, written as a select tree on its bits so that the compiler keeps
+  // the chunk in registers instead of indexing it through memory.
+  __device__ __forceinline__ float get_dyn(int e) const {
+    const uint32_t lo = (e & 2) ? v.y : v.x;
+    const uint32_t hi = (e & 2) ? v.w : v.z;
+    const uint32_t d = (e & 4) ? hi : lo;
     return (e & 1) ? bf16_hi(d) : bf16_lo(d);
   }
 };
@@ -122,7 +136,18 @@ struct Chunk<float, 4> {
   float4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
   __device__ __forceinline__ void fill_neg_inf() { v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
+  __device__ __forceinline__ void select_if(bool c, const Chunk& o) {
+    v.x = c ? o.v.x : v.x;
+    v.y = c ? o.v.y : v.y;
+    v.z = c ? o.v.z : v.z;
+    v.w = c ? o.v.w : v.w;
+  }
   __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+  __device__ __forceinline__ float get_dyn(int e) const {
+    const float lo = (e & 1) ? v.y : v.x;
+    const float hi = (e & 1) ? v.w : v.z;
+    return (e & 2) ? hi : lo;
+  }
 };
 
 template <>
@@ -131,7 +156,9 @@ struct Chunk<uint16_t, 1> {
   uint32_t v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *p; }
   __device__ __forceinline__ void fill_neg_inf() { v = 0xFF80u; }
+  __device__ __forceinline__ void select_if(bool c, const Chunk& o) { v = c ? o.v : v; }
   __device__ __forceinline__ float get(int) const { return bf16_lo(v); }
+  __device__ __forceinline__ float get_dyn(int) const { return bf16_lo(v); }
 };
 
 template <>
@@ -140,7 +167,9 @@ struct Chunk<float, 1> {
   float v;
   __device__ __forceinline__ void load(const float* p) { v = *p; }
   __device__ __forceinline__ void fill_neg_inf() { v = -INFINITY; }
+  __device__ __forceinline__ void select_if(bool c, const Chunk& o) { v = c ? o.v : v; }
   __device__ __forceinline__ float get(int) const { return v; }
+  __device__ __forceinline__ float get_dyn(int) const { return v; }
 };
 
 __device__ __forceinline__ float logit_at(const void* base, int dtype, int64_t idx) {
@@ -204,36 +233,48 @@ __device__ __forceinline__ void wave_best(double& k, int& i) {
   }
 }
 
-// Two best fp32 keys of a slice, k1 >= k2, equal keys ordered by lower index.
+// Two best fp32 keys seen by a lane or a wave, k1 >= k2, equal keys ordered by
+// lower index. Each entry carries the two logits its key came from, so the
+// winners can be re-evaluated in fp64 without reloading them.
 struct Top2 {
   float k1, k2;
   int i1, i2;
+  float a1, b1, a2, b2;
 };
 
-__device__ __forceinline__ Top2 top2_empty() { return Top2{-1.0f, -1.0f, INT32_MAX, INT32_MAX}; }
+__device__ __forceinline__ Top2 top2_empty() {
+  return Top2{-INFINITY, -INFINITY, INT32_MAX, INT32_MAX, 0.0f, 0.0f, 0.0f, 0.0f};
+}
 
-__device__ __forceinline__ void top2_push(Top2& t, float k, int i) {
+__device__ __forceinline__ void top2_push(Top2& t, float k, int i, float a, float b) {
   if (k > t.k1 || (k == t.k1 && i < t.i1)) {
     t.k2 = t.k1;
     t.i2 = t.i1;
+    t.a2 = t.a1;
+    t.b2 = t.b1;
     t.k1 = k;
     t.i1 = i;
+    t.a1 = a;
+    t.b1 = b;
   } else if (k > t.k2 || (k == t.k2 && i < t.i2)) {
     t.k2 = k;
     t.i2 = i;
+    t.a2 = a;
+    t.b2 = b;
   }
 }
 
 __device__ __forceinline__ void wave_top2(Top2& t) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const float a1 = __shfl_xor(t.k1, o), a2 = __shfl_xor(t.k2, o);
-    const int j1 = __shfl_xor(t.i1, o), j2 = __shfl_xor(t.i2, o);
-    top2_push(t, a1, j1);
-    top2_push(t, a2, j2);
+    const float k1 = __shfl_xor(t.k1, o), k2 = __shfl_xor(t.k2, o);
+    const int i1 = __shfl_xor(t.i1, o), i2 = __shfl_xor(t.i2, o);
+    const float a1 = __shfl_xor(t.a1, o), b1 = __shfl_xor(t.b1, o);
+    const float a2 = __shfl_xor(t.a2, o), b2 = __shfl_xor(t.b2, o);
+    top2_push(t, k1, i1, a1, b1);
+    top2_push(t, k2, i2, a2, b2);
   }
 }
-
 
 // ------------------------------------------------------------------ hand-off between workgroups
 // A record that one wave writes and another wave (maybe on another XCD) reads in the same
@@ -249,56 +290,29 @@ __device__ __forceinline__ uint32_t load_word(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void publish(P1Part* dst, const P1Part& v) {
+template <int N>
+struct Words {
+  uint32_t w[N];
+};
+
+template <class T>
+__device__ __forceinline__ void publish(T* dst, const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "records are made of 4-byte words");
+  constexpr int n = sizeof(T) / 4;
+  const Words<n> w = __builtin_bit_cast(Words<n>, v);
   uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-  store_word(d + 0, __float_as_uint(v.m_t));
-  store_word(d + 1, __float_as_uint(v.s_t));
-  store_word(d + 2, __float_as_uint(v.m_d));
-  store_word(d + 3, __float_as_uint(v.s_d));
-  store_word(d + 4, (uint32_t)v.am_t);
-  store_word(d + 5, (uint32_t)v.am_d);
-  store_word(d + 6, (uint32_t)v.bad);
-  store_word(d + 7, (uint32_t)v.pad);
+#pragma unroll
+  for (int i = 0; i < n; ++i) store_word(d + i, w.w[i]);
 }
 
-__device__ __forceinline__ P1Part read_p1(const P1Part* src) {
+template <class T>
+__device__ __forceinline__ T read_record(const T* src) {
+  constexpr int n = sizeof(T) / 4;
+  Words<n> w;
   const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
-  P1Part v;
-  v.m_t = __uint_as_float(load_word(s + 0));
-  v.s_t = __uint_as_float(load_word(s + 1));
-  v.m_d = __uint_as_float(load_word(s + 2));
-  v.s_d = __uint_as_float(load_word(s + 3));
-  v.am_t = (int32_t)load_word(s + 4);
-  v.am_d = (int32_t)load_word(s + 5);
-  v.bad = (int32_t)load_word(s + 6);
-  v.pad = 0;
-  return v;
-}
-
-__device__ __forceinline__ void publish(P2Part* dst, const P2Part& v) {
-  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-  store_word(d + 0, __float_as_uint(v.k1));
-  store_word(d + 1, __float_as_uint(v.k2));
-  store_word(d + 2, (uint32_t)v.i1);
-  store_word(d + 3, (uint32_t)v.i2);
-  store_word(d + 4, __float_as_uint(v.rsum));
-  store_word(d + 5, __float_as_uint(v.mref));
-  store_word(d + 6, (uint32_t)v.bad);
-  store_word(d + 7, (uint32_t)v.gidx);
-}
-
-__device__ __forceinline__ P2Part read_p2(const P2Part* src) {
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
-  P2Part v;
-  v.k1 = __uint_as_float(load_word(s + 0));
-  v.k2 = __uint_as_float(load_word(s + 1));
-  v.i1 = (int32_t)load_word(s + 2);
-  v.i2 = (int32_t)load_word(s + 3);
-  v.rsum = __uint_as_float(load_word(s + 4));
-  v.mref = __uint_as_float(load_word(s + 5));
-  v.bad = (int32_t)load_word(s + 6);
-  v.gidx = (int32_t)load_word(s + 7);
-  return v;
+#pragma unroll
+  for (int i = 0; i < n; ++i) w.w[i] = load_word(s + i);
+  return __builtin_bit_cast(T, w);
 }
 
 // Arrive at a counter shared by `total` waves. Returns true in the wave that arrives last.

@@ -30,36 +30,41 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   q.V = s.V;
   q.dtype = s.dtype;
   q.esize = s.dtype == SV_BF16 ? 2 : 4;
-  // Long-lived waves: each one streams a contiguous span of a row. Pass 1 aims
-  // at about 3072 waves (3 per SIMD on 256 CUs) so that one round of waves
-  // covers the rows; pass 2 at about 4096. A row is never split into spans
-  // shorter than 8192 logits.
-  const int64_t max_split = s.V / 8192 > 1 ? s.V / 8192 : 1;
-  const int64_t want1 = s.R > 0 ? ceil_div(768, s.R) : 1;
-  const int64_t want2 = s.B > 0 ? ceil_div(1024, s.B) : 1;
-  q.s1 = (int32_t)(want1 < max_split ? want1 : max_split);
-  q.s2 = (int32_t)(want2 < max_split ? want2 : max_split);
-  if ((int64_t)q.R * q.s1 > INT32_MAX || (int64_t)q.B * q.s2 > INT32_MAX) return SV_E_UNSUPPORTED;
+  // Waves stream contiguous spans of a row. Pass 1 gives a wave at least two
+  // batches of each array; pass 2 about one. A row has at most 64 waves, so that a
+  // pass-2 wave can hold one row's partials.
+  const int64_t row_bytes = (int64_t)s.V * q.esize;
+  int64_t w1 = row_bytes / (2 * kBatchBytes1);
+  int64_t w2 = ceil_div(row_bytes, kBatchBytes2);
+  q.w1max = (int32_t)(w1 < 1 ? 1 : w1 > kMaxWavesPerRow ? kMaxWavesPerRow : w1);
+  q.w2max = (int32_t)(w2 < 1 ? 1 : w2 > kMaxWavesPerRow ? kMaxWavesPerRow : w2);
+  if ((int64_t)q.R * q.w1max > INT32_MAX || (int64_t)q.B * q.w2max > INT32_MAX) return SV_E_UNSUPPORTED;
   size_t off = 0;
   q.off_hdr = off;
   off += sizeof(WsHeader);
   q.off_part1 = off = align_up(off, 256);
-  off += (size_t)q.R * q.s1 * kWavesPerBlock * sizeof(P1Part);
-  q.off_rec = off = align_up(off, 256);
-  off += (size_t)q.R * sizeof(RowRec);
-  q.off_desc = off = align_up(off, 256);
-  off += (size_t)q.B * sizeof(ReqDesc);
+  off += (size_t)q.R * q.w1max * sizeof(P1Part);
   q.off_part2 = off = align_up(off, 256);
-  off += (size_t)q.B * q.s2 * kWavesPerBlock * sizeof(P2Part);
-  q.off_ticket_row = off = align_up(off, 256);
-  off += (size_t)q.R * sizeof(uint32_t);
-  q.off_ticket_req = off = align_up(off, 256);
-  off += (size_t)q.B * sizeof(uint32_t);
+  off += (size_t)q.B * q.w2max * sizeof(P2Part);
   q.off_ticket2 = off = align_up(off, 256);
   off += (size_t)q.B * sizeof(uint32_t);
   q.total = align_up(off, 256);
   *p = q;
   return SV_OK;
+}
+
+Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2) {
+  Launch l{};
+  // Pass 1 streams the proposal rows: every row but the last of each request, unless a
+  // request stops early. The other rows' waves exit after classifying their row.
+  const int64_t rows = p.R - p.B > 0 ? p.R - p.B : 1;
+  int64_t w1 = slots1 / rows;
+  int64_t w2 = p.B > 0 ? slots2 / p.B : 1;
+  l.w1 = (int32_t)(w1 < 1 ? 1 : w1 > p.w1max ? p.w1max : w1);
+  l.w2 = (int32_t)(w2 < 1 ? 1 : w2 > p.w2max ? p.w2max : w2);
+  l.blocks1 = ceil_div((int64_t)p.R * l.w1, kWavesPerBlock);
+  l.blocks2 = ceil_div((int64_t)p.B * l.w2, kWavesPerBlock);
+  return l;
 }
 
 sv_status check_call(const sv_shape& shape, const void* target, const void* draft,

@@ -101,6 +101,11 @@ __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d 
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
 // VEC logits held as one load. bf16 logits arrive as raw 16-bit patterns.
+// load_nt marks the load non-temporal: logits that one kernel reads once are streamed
+// past the caches instead of displacing lines that are reused.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <typename E, int VEC>
 struct Chunk;
 
@@ -109,6 +114,10 @@ struct Chunk<uint16_t, 8> {
   static constexpr int kVec = 8;
   uint4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_nt(const uint16_t* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v = make_uint4(t.x, t.y, t.z, t.w);
+  }
   __device__ __forceinline__ void fill_neg_inf() { v = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
   __device__ __forceinline__ void select_if(bool c, const Chunk& o) {
     v.x = c ? o.v.x : v.x;
@@ -135,6 +144,10 @@ struct Chunk<float, 4> {
   static constexpr int kVec = 4;
   float4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    v = make_float4(t.x, t.y, t.z, t.w);
+  }
   __device__ __forceinline__ void fill_neg_inf() { v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
   __device__ __forceinline__ void select_if(bool c, const Chunk& o) {
     v.x = c ? o.v.x : v.x;
@@ -155,6 +168,7 @@ struct Chunk<uint16_t, 1> {
   static constexpr int kVec = 1;
   uint32_t v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *p; }
+  __device__ __forceinline__ void load_nt(const uint16_t* p) { v = __builtin_nontemporal_load(p); }
   __device__ __forceinline__ void fill_neg_inf() { v = 0xFF80u; }
   __device__ __forceinline__ void select_if(bool c, const Chunk& o) { v = c ? o.v : v; }
   __device__ __forceinline__ float get(int) const { return bf16_lo(v); }
@@ -166,11 +180,15 @@ struct Chunk<float, 1> {
   static constexpr int kVec = 1;
   float v;
   __device__ __forceinline__ void load(const float* p) { v = *p; }
+  __device__ __forceinline__ void load_nt(const float* p) { v = __builtin_nontemporal_load(p); }
   __device__ __forceinline__ void fill_neg_inf() { v = -INFINITY; }
   __device__ __forceinline__ void select_if(bool c, const Chunk& o) { v = c ? o.v : v; }
   __device__ __forceinline__ float get(int) const { return v; }
   __device__ __forceinline__ float get_dyn(int) const { return v; }
 };
+
+__device__ __forceinline__ float to_float(uint16_t v) { return bf16_lo((uint32_t)v); }
+__device__ __forceinline__ float to_float(float v) { return v; }
 
 __device__ __forceinline__ float logit_at(const void* base, int dtype, int64_t idx) {
   if (dtype == SV_BF16) return bf16_lo((uint32_t) reinterpret_cast<const uint16_t*>(base)[idx]);

@@ -2,9 +2,9 @@
 //
 // The record types below live in the caller's workspace. Their layouts are
 // fixed here so that the kernels and the host-side size computation agree.
-// Records that one wave writes and another reads inside the same kernel move
-// word by word with agent-scope atomics, so every field is 4-byte sized
-// (doubles are split into two words).
+// Pass 1's partials reach pass 2 across the kernel boundary. Pass 2's partials
+// move between its own workgroups word by word with agent-scope atomics, so
+// their fields are 4-byte words (a double counts as two).
 #pragma once
 
 #include <stddef.h>
@@ -17,14 +17,19 @@ namespace sv {
 constexpr int kWave = 64;                       // CDNA wavefront width
 constexpr int kBlock = 256;                     // threads per workgroup in every kernel
 constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kMaxWavesPerRow = 64;             // pass-2 walks hold one row's partials in a wave
+// Bytes of one array that a wave requests per loop step: pass 1 keeps two such batches
+// per array in flight (double buffering), pass 2 one larger batch.
+constexpr int kBatchBytes1 = 3 * kWave * 16;
+constexpr int kBatchBytes2 = 6 * kWave * 16;
 
-// Row verdict kept in RowRec besides the public SV_ROW_* codes.
+// Row verdict used inside the kernels besides the public SV_ROW_* codes.
 enum : int32_t { kRowInvalid = 5 };
 
 // What pass 2 does for a request.
 enum : int32_t {
-  kKindInvalid = 0,      // failed closed (emitted by pass 1)
-  kKindGreedyDone = 1,   // greedy, stopped on a proposal row: token = that row's argmax (emitted by pass 1)
+  kKindInvalid = 0,      // failed closed
+  kKindGreedyDone = 1,   // greedy, stopped on a proposal row: token = that row's argmax
   kKindResidual = 2,     // race over (p - mu)+ on the stop row
   kKindBonus = 3,        // race over p on the bonus row
   kKindGreedyBonus = 4   // argmax of the bonus row
@@ -43,34 +48,6 @@ struct P1Part {
   int32_t pad[3];
 };
 static_assert(sizeof(P1Part) == 48, "P1Part layout");
-
-// Pass 1: the row's merged statistics and verdict, written by the wave that finalises the row.
-struct RowRec {
-  int32_t verdict;  // SV_ROW_ACCEPT / REJECT / NULL, or kRowInvalid
-  int32_t am_t;     // greedy rows: row target argmax (lowest index)
-  int32_t am_d;     // greedy rows: row draft argmax
-  float c;          // log2(e)/T rounded to fp32: the scale every kernel uses
-  float m_t, mc_t;  // row max target logit and fl(m_t*c)
-  float m_d, mc_d;  // row max draft logit and fl(m_d*c)
-  uint32_t s_t_lo, s_t_hi;  // fp64 row sums of exp2(l*c - mc), split into words
-  uint32_t s_d_lo, s_d_hi;
-  float p_D, q_D, mu_D, u;
-  int32_t pad[4];
-};
-static_assert(sizeof(RowRec) == 80, "RowRec layout");
-
-// Pass 1 -> pass 2: what the request needs for its last token.
-struct ReqDesc {
-  int32_t kind;           // kKind*
-  int32_t k;              // accepted drafts
-  int32_t f;              // row that draws the last token
-  int32_t final_verdict;  // SV_ROW_REJECT / NULL / BONUS
-  float T, tau, c, mc_t;
-  float mc_d, m_t, pad0, pad2;
-  double s_t, s_d;        // residual rows: row sums
-  int32_t pad1[4];
-};
-static_assert(sizeof(ReqDesc) == 80, "ReqDesc layout");
 
 // Pass 2: one partial per (request, wave).
 struct P2Part {
@@ -93,15 +70,24 @@ static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 struct Plan {
   int32_t B, R, V, dtype;
   int32_t esize;  // bytes per logit
-  int32_t s1;     // pass 1: workgroups per row (4 waves each)
-  int32_t s2;     // pass 2: workgroups per request
-  size_t off_hdr, off_part1, off_rec, off_desc, off_part2, off_ticket_row, off_ticket_req,
-      off_ticket2, total;
+  int32_t w1max;  // pass 1: most waves that share one row (sizes the partial array)
+  int32_t w2max;  // pass 2: most waves that share one request
+  size_t off_hdr, off_part1, off_part2, off_ticket2, total;
 };
 
 // Build the plan for a shape. Returns SV_OK, or the status describing why the
 // shape cannot be served. Host-only, allocation-free.
 sv_status make_plan(const sv_shape& shape, Plan* out);
+
+// Waves per row in pass 1 (w1) and per request in pass 2 (w2), and the grids.
+struct Launch {
+  int32_t w1, w2;
+  int64_t blocks1, blocks2;
+};
+
+// Choose the split for a device on which each kernel keeps `slots1` / `slots2` waves
+// resident: one round of waves covers the work, and no split exceeds the plan's bounds.
+Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2);
 
 // Validate every host-checkable argument of a verify call.
 sv_status check_call(const sv_shape& shape, const void* target, const void* draft,

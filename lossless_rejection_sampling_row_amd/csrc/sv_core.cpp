@@ -30,14 +30,11 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   q.V = s.V;
   q.dtype = s.dtype;
   q.esize = s.dtype == SV_BF16 ? 2 : 4;
-  // Waves stream contiguous spans of a row. Pass 1 gives a wave at least two
-  // batches of each array; pass 2 about one. A row has at most 64 waves, so that a
-  // pass-2 wave can hold one row's partials.
+  // Waves stream contiguous spans of a row, at least two batches of each array per wave.
+  // A row has at most 64 waves, so that a pass-2 wave can hold one row's partials.
   const int64_t row_bytes = (int64_t)s.V * q.esize;
-  int64_t w1 = row_bytes / (2 * kBatchBytes1);
-  int64_t w2 = ceil_div(row_bytes, kBatchBytes2);
-  q.w1max = (int32_t)(w1 < 1 ? 1 : w1 > kMaxWavesPerRow ? kMaxWavesPerRow : w1);
-  q.w2max = (int32_t)(w2 < 1 ? 1 : w2 > kMaxWavesPerRow ? kMaxWavesPerRow : w2);
+  const int64_t w = row_bytes / (2 * kBatchBytes);
+  q.w1max = q.w2max = (int32_t)(w < 1 ? 1 : w > kMaxWavesPerRow ? kMaxWavesPerRow : w);
   if ((int64_t)q.R * q.w1max > INT32_MAX || (int64_t)q.B * q.w2max > INT32_MAX) return SV_E_UNSUPPORTED;
   size_t off = 0;
   q.off_hdr = off;
@@ -55,14 +52,19 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
 
 Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2) {
   Launch l{};
-  // Pass 1 streams the proposal rows: every row but the last of each request, unless a
-  // request stops early. The other rows' waves exit after classifying their row.
-  const int64_t rows = p.R - p.B > 0 ? p.R - p.B : 1;
-  int64_t w1 = slots1 / rows;
+  // Pass 1 streams the potential proposal rows: every row but the last of each request.
+  // Pass 2 merges a row's partials in aligned lane groups, so the waves per row are a
+  // power of two.
+  const int64_t rows = p.R - p.B;
+  int64_t w1 = rows > 0 ? slots1 / rows : 1;
+  if (w1 > p.w1max) w1 = p.w1max;
+  int64_t pow2 = 1;
+  while (pow2 * 2 <= w1) pow2 *= 2;
   int64_t w2 = p.B > 0 ? slots2 / p.B : 1;
-  l.w1 = (int32_t)(w1 < 1 ? 1 : w1 > p.w1max ? p.w1max : w1);
+  l.w1 = (int32_t)pow2;
   l.w2 = (int32_t)(w2 < 1 ? 1 : w2 > p.w2max ? p.w2max : w2);
-  l.blocks1 = ceil_div((int64_t)p.R * l.w1, kWavesPerBlock);
+  l.blocks1 = ceil_div(rows * l.w1, kWavesPerBlock);
+  if (l.blocks1 < 1) l.blocks1 = 1;  // block 0 checks row_offsets even when nothing is streamed
   l.blocks2 = ceil_div((int64_t)p.B * l.w2, kWavesPerBlock);
   return l;
 }

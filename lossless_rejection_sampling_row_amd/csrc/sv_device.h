@@ -234,6 +234,40 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
+// Reductions over aligned groups of `width` lanes (a power of two, at most 64): every lane
+// ends with its group's result, combined in a fixed order.
+__device__ __forceinline__ float seg_max(float x, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float seg_sum(float x, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ double seg_sum(double x, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int seg_min(int x, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+
+// A value every lane of the wave holds alike, moved to a scalar register.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ __forceinline__ double uni(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Best (key, index) under "larger key wins, then lower index".
 __device__ __forceinline__ bool beats(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);

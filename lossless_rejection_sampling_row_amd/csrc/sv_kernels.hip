@@ -96,59 +96,64 @@ __device__ __forceinline__ float fold_scale(float T) { return T == 0.0f ? 1.0f :
 
 // ====================================================================== pass 1
 
+// Pass 1 streams the potential proposal rows: every row but the last of its request. Slot
+// p of the pass-1 grid is the p-th of them, row r = p + b of request b, where b is the
+// largest request index with ro[b] - b <= p.
 struct RowCls {
-  bool located;   // row r lies in a well-formed request range
-  bool req_ok;    // temperature and tau are valid
-  bool proposal;  // row r is tested by the method (j < n_prop)
-  int b, lo, n, j;
-  int n_prop;     // leading rows before the request's first no-proposal row (and before its last row)
-  int D;
+  bool proposal;  // the slot's row is tested by the method
+  int r;          // the row, always inside [0, R)
+  int b, lo, j;   // request, its first row, and r's position in it
+  int D;          // drafted token of row r
   float T, tau;
 };
 
-// Locate row r's request and classify it. Every index stays in bounds whatever
-// row_offsets holds. A broken batch is caught by block 0's check and failed
+// The slot's request when every request has the same number of rows.
+__device__ __forceinline__ int slot_guess(const Inputs& in, int p) {
+  const int np = in.R - in.B;
+  return min((int)(((int64_t)p * in.B) / np), in.B - 1);
+}
+
+// Classify slot p in one round trip when the guess holds: the request's range, temperature
+// and tau, and the drafted tokens of the 64 rows ending at r are requested together. A
+// wrong guess (requests of different lengths) costs a binary search. Every index stays in
+// bounds whatever row_offsets holds; a broken batch is caught by block 0's check and fails
 // closed in pass 2.
-__device__ RowCls classify_row(const Inputs& in, int r, int lane) {
+__device__ RowCls classify_slot(const Inputs& in, int p, int b, int lane) {
   RowCls c{};
-  int b = (int)(((int64_t)r * in.B) / in.R);
-  if (b >= in.B) b = in.B - 1;
   int lo = in.ro[b], hi = in.ro[b + 1];
-  if (!(lo <= r && r < hi)) {
-    int L = 0, H = in.B - 1;  // largest b with ro[b] <= r
+  float T = in.temp[b], tau = in.tau[b];
+  int r = min(max(p + b, 0), in.R - 1);
+  int dwin = in.dt[max(r - lane, 0)];  // lane i: drafted token of row r - i
+  if (!(lo <= p + b && p + b < hi - 1)) {
+    int L = 0, H = in.B - 1;  // largest b with ro[b] - b <= p
     while (L < H) {
       const int mid = (L + H + 1) >> 1;
-      if (in.ro[mid] <= r) L = mid; else H = mid - 1;
+      if (in.ro[mid] - mid <= p) L = mid; else H = mid - 1;
     }
     b = L;
     lo = in.ro[b];
     hi = in.ro[b + 1];
+    T = in.temp[b];
+    tau = in.tau[b];
+    r = min(max(p + b, 0), in.R - 1);
+    dwin = in.dt[max(r - lane, 0)];
   }
-  c.located = 0 <= lo && lo <= r && r < hi && hi <= in.R;
-  if (!c.located) return c;
+  c.r = r;
+  if (!(0 <= lo && lo <= p + b && p + b < hi - 1 && hi <= in.R)) return c;
   c.b = b;
   c.lo = lo;
-  c.n = hi - lo;
   c.j = r - lo;
-  c.T = in.temp[b];
-  c.tau = in.tau[b];
-  c.req_ok = temperature_ok(c.T) && !__builtin_isnan(c.tau);
-  c.n_prop = c.n - 1;
-  for (int base = 0; base < c.n - 1; base += kWave) {
-    const int i = base + lane;
-    bool badtok = false;
-    if (i < c.n - 1) {
-      const int D = in.dt[lo + i];
-      badtok = D < 0 || D >= in.V;
-    }
-    const uint64_t m = __ballot(badtok);
-    if (m != 0) {
-      c.n_prop = base + __ffsll((unsigned long long)m) - 1;
-      break;
-    }
+  c.T = T;
+  c.tau = tau;
+  // Rows lo..r must all carry a drafted token in [0, V): the request stops at the first
+  // row without one.
+  bool bad = lane <= c.j && (dwin < 0 || dwin >= in.V);
+  c.D = __shfl(dwin, 0);
+  for (int base = kWave; base <= c.j && !__ballot(bad); base += kWave) {  // windows beyond 64 rows
+    const int D = in.dt[max(r - base - lane, 0)];
+    bad = base + lane <= c.j && (D < 0 || D >= in.V);
   }
-  c.proposal = c.req_ok && c.j < c.n_prop;
-  c.D = c.proposal ? in.dt[r] : -1;
+  c.proposal = temperature_ok(T) && !__builtin_isnan(tau) && __ballot(bad) == 0;
   return c;
 }
 
@@ -314,8 +319,8 @@ __device__ void block0_duties(const Inputs& in, const Work& w, const Outputs& ou
 
 
 
-// Waves, not workgroups, are assigned to rows: wave gw of the grid streams span gw % w1 of
-// row gw / w1, so the split need not be a multiple of a workgroup's four waves.
+// Waves, not workgroups, are assigned to slots: wave gw of the grid streams span gw % w1 of
+// slot gw / w1, so the split need not be a multiple of a workgroup's four waves.
 template <typename E, int VEC, int U>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void pass1_kernel(Inputs in, Work w,
                                                                                              Outputs out) {
@@ -323,25 +328,37 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (blockIdx.x == 0) block0_duties(in, w, out);
-  const int r = (int)min(gw / in.w1, (int64_t)in.R - 1);
+  const int np = in.R - in.B;
+  if (gw >= (int64_t)np * in.w1) return;
+  const int p = (int)(gw / in.w1);
   const int g = (int)(gw % in.w1);
-  const bool in_grid = gw < (int64_t)in.R * in.w1;
 
   using CH = Chunk<E, VEC>;
   const int nvec = in.V / VEC;
   const Span sp = wave_span(nvec, in.w1, g);
-  const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
-  const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
+  const int bg = slot_guess(in, p);
+  const int rg = min(p + bg, in.R - 1);
+  const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)rg * in.V;
+  const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)rg * in.V;
   constexpr int step = U * kWave;
   CH ta[U], da[U], tb[U], db[U];
-  // The first batch is requested before the row is classified, so the row's metadata and
-  // its first logits arrive together. A row the method does not test drops them.
+  // The first batch of the guessed row is requested before the slot is classified, so the
+  // row's metadata and its first logits arrive together.
   if (sp.begin < sp.end) {
     load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
     load_chunks<true>(da, drow, sp.begin, lane, sp.end);
   }
-  const RowCls cls = classify_row(in, r, lane);
-  if (!in_grid || !cls.proposal) return;
+  const RowCls cls = classify_slot(in, p, bg, lane);
+  if (!cls.proposal) return;
+  const int r = cls.r;
+  if (r != rg) {  // the guess missed: stream the right row
+    trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
+    drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
+    if (sp.begin < sp.end) {
+      load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
+      load_chunks<true>(da, drow, sp.begin, lane, sp.end);
+    }
+  }
 
   const bool greedy = cls.T == 0.0f;
   const float c = fold_scale(cls.T);
@@ -418,52 +435,40 @@ struct RowEval {
   float p_D, q_D, mu_D, u;
 };
 
-// Merge row j's partials and test its drafted token D. The wave's lanes hold the row's
-// partials: slot 0 of a lane when m0 is set, slot 1 when m1 is set. The statistics are
-// merged in a fixed order with fp64 sums, and every lane ends with the same result.
-__device__ __forceinline__ RowEval eval_row(const Inputs& in, const P1Part& e0, const P1Part& e1, bool m0,
-                                            bool m1, int b, int j, int D, float T, float tau, float c,
-                                            RowStat& rs) {
+// Merge the partials of the rows held by this wave and test each row's drafted token, all
+// rows at once. Row jj of the set sits in the aligned group of nw lanes starting at jj*nw
+// (nw, the waves per row, is a power of two), one partial per lane; `live` marks lanes
+// whose row is to be tested. Each group reduces in a fixed order with fp64 sums, so every
+// lane of a group ends with its row's result. j is the lane's row position in the request
+// and D its drafted token.
+__device__ __forceinline__ RowEval eval_rows(const Inputs& in, const P1Part& e, bool live, int nw, int b, int j,
+                                             int D, float T, float tau, float c, RowStat& rs) {
   const bool greedy = T == 0.0f;
-  float mt = -INFINITY, md = -INFINITY;
-  if (m0) {
-    mt = e0.m_t;
-    md = e0.m_d;
-  }
-  if (m1) {
-    mt = fmaxf(mt, e1.m_t);
-    md = fmaxf(md, e1.m_d);
-  }
-  mt = wave_max(mt);
-  md = wave_max(md);
+  const float mt = seg_max(live ? e.m_t : -INFINITY, nw);
+  const float md = seg_max(live ? e.m_d : -INFINITY, nw);
   const float mct = ref_of(mt, c), mcd = ref_of(md, c);
   double st = 0.0, sd = 0.0;
   int it = INT32_MAX, id = INT32_MAX;
-  if (m0) {
-    if (e0.s_t != 0.0f) st += (double)(e0.s_t * fast_exp2(ref_of(e0.m_t, c) - mct));
-    if (e0.s_d != 0.0f) sd += (double)(e0.s_d * fast_exp2(ref_of(e0.m_d, c) - mcd));
-    if (e0.m_t == mt && e0.am_t >= 0) it = e0.am_t;
-    if (e0.m_d == md && e0.am_d >= 0) id = e0.am_d;
+  if (live) {
+    if (e.s_t != 0.0f) st = (double)(e.s_t * fast_exp2(ref_of(e.m_t, c) - mct));
+    if (e.s_d != 0.0f) sd = (double)(e.s_d * fast_exp2(ref_of(e.m_d, c) - mcd));
+    if (e.m_t == mt && e.am_t >= 0) it = e.am_t;
+    if (e.m_d == md && e.am_d >= 0) id = e.am_d;
   }
-  if (m1) {
-    if (e1.s_t != 0.0f) st += (double)(e1.s_t * fast_exp2(ref_of(e1.m_t, c) - mct));
-    if (e1.s_d != 0.0f) sd += (double)(e1.s_d * fast_exp2(ref_of(e1.m_d, c) - mcd));
-    if (e1.m_t == mt && e1.am_t >= 0) it = min(it, e1.am_t);
-    if (e1.m_d == md && e1.am_d >= 0) id = min(id, e1.am_d);
-  }
-  st = wave_sum(st);
-  sd = wave_sum(sd);
-  it = wave_min(it);
-  id = wave_min(id);
-  const bool f0 = m0 && (e0.flags & 2), f1 = m1 && (e1.flags & 2);
-  const uint64_t fm = __ballot(f0 || f1);
-  const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
-  const float ltD = __shfl(f0 ? e0.lt_D : e1.lt_D, src);
-  const float ldD = __shfl(f0 ? e0.ld_D : e1.ld_D, src);
+  st = seg_sum(st, nw);
+  sd = seg_sum(sd, nw);
+  it = seg_min(it, nw);
+  id = seg_min(id, nw);
+  // Exactly one partial of a row holds the drafted token's logits: the group sums pick
+  // them up unchanged (x + 0 = x).
+  const bool f = live && (e.flags & 2);
+  const float ltD = seg_sum(f ? e.lt_D : 0.0f, nw);
+  const float ldD = seg_sum(f ? e.ld_D : 0.0f, nw);
+  const int nf = __float2int_rn(seg_sum(f ? 1.0f : 0.0f, nw));
   rs = RowStat{mt, mct, md, mcd, st, sd, it == INT32_MAX ? -1 : it, id == INT32_MAX ? -1 : id};
 
   const bool valid = __builtin_isfinite(mt) && __builtin_isfinite(md) && __builtin_isfinite(st) && st > 0.0 &&
-                     __builtin_isfinite(sd) && sd > 0.0;
+                     __builtin_isfinite(sd) && sd > 0.0 && nf == 1;
   RowEval ev{};
   ev.u = NAN;
   if (greedy) {
@@ -482,7 +487,7 @@ __device__ __forceinline__ RowEval eval_row(const Inputs& in, const P1Part& e0, 
   ev.p_D = (float)p;
   ev.q_D = (float)q;
   ev.mu_D = (float)mu;
-  if (!valid || fm == 0) {
+  if (!valid) {
     ev.verdict = kRowInvalid;
   } else if (!offered) {
     ev.verdict = SV_ROW_NULL;
@@ -494,7 +499,39 @@ __device__ __forceinline__ RowEval eval_row(const Inputs& in, const P1Part& e0, 
   return ev;
 }
 
-// A request as pass 2 rebuilds it.
+// Field-by-field choice between two register-held partials (a reference to either of two
+// locals would move both to memory).
+__device__ __forceinline__ P1Part pick_part(bool second, const P1Part& a, const P1Part& b) {
+  P1Part r;
+  r.m_t = second ? b.m_t : a.m_t;
+  r.s_t = second ? b.s_t : a.s_t;
+  r.m_d = second ? b.m_d : a.m_d;
+  r.s_d = second ? b.s_d : a.s_d;
+  r.am_t = second ? b.am_t : a.am_t;
+  r.am_d = second ? b.am_d : a.am_d;
+  r.flags = second ? b.flags : a.flags;
+  r.lt_D = second ? b.lt_D : a.lt_D;
+  r.ld_D = second ? b.ld_D : a.ld_D;
+  r.pad[0] = r.pad[1] = r.pad[2] = 0;
+  return r;
+}
+
+// A request's range, temperature and tau: one round trip.
+struct ReqHead {
+  int lo, n;
+  float T, tau;
+};
+
+__device__ __forceinline__ ReqHead request_head(const Inputs& in, int b) {
+  ReqHead h;
+  h.lo = in.ro[b];
+  h.n = in.ro[b + 1] - h.lo;
+  h.T = in.temp[b];
+  h.tau = in.tau[b];
+  return h;
+}
+
+// A request as pass 2 rebuilds it. Every field is wave-uniform.
 struct ReqState {
   int lo, n, n_prop;
   int k;              // accepted drafts
@@ -503,40 +540,47 @@ struct ReqState {
   int final_verdict;  // verdict of row f (SV_ROW_BONUS when every proposal row was accepted)
   float T, tau, c;
   RowStat stop;       // row f's statistics when f is a proposal row
-  int stop_slot;      // row f's index within the partial group held in e0/e1
+  int stop_half;      // row f's partials are in e1 (1) or e0 (0) ...
+  int stop_lane0;     // ... in lanes stop_lane0 .. stop_lane0 + w1 - 1
 };
 
-// Rebuild request b from the inputs and pass 1's partials: walk its proposal rows in
-// order up to the first one that is not accepted. Every wave of the request does this on
-// its own, so no wave waits for another.
-//  - Round trip 1: the request's row range, temperature and tau.
-//  - Round trip 2: the drafted tokens of its first 64 rows and the partials of its first
-//    128 / (waves per row) rows, fetched together into two slots per lane (e0, e1).
-// On return e0/e1 hold the group of partials that contains row f. With `diag`, each row's
-// record is written once: tested rows by lane 0 in the walk (the stop row with
-// `stop_resid`), untested and bonus rows after it.
-__device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w, int b, int lane,
-                                                 P1Part& e0, P1Part& e1, sv_row_diag* diag,
-                                                 float stop_resid) {
+// The drafted tokens of rows lo .. lo+63 (lane j: row lo + j) and the pass-1 partials of
+// rows lo .. lo + 128/w1 - 1 in two slots per lane: e0 holds rows lo .. lo + 64/w1 - 1,
+// e1 the next 64/w1 rows, one partial per lane. Indices are clamped into the arrays, so
+// this may run before lo is known to be right.
+__device__ __forceinline__ void prefetch_rows(const Inputs& in, const Work& w, int lo, int lane, int& dt0,
+                                              P1Part& e0, P1Part& e1) {
+  dt0 = in.dt[min(lo + lane, in.R - 1)];
+  const int64_t base = (int64_t)lo * in.w1;
+  const int64_t last = (int64_t)in.R * in.w1 - 1;
+  e0 = w.part1[min(base + lane, last)];
+  e1 = w.part1[min(base + lane + kWave, last)];
+}
+
+// Rebuild request b (head h, row_offsets checked) from the inputs and pass 1's partials:
+// test its proposal rows in order up to the first one that is not accepted. Every wave of
+// the request does this on its own, so no wave waits for another. dt0/e0/e1 arrive
+// prefetched for first row lo_pre (fetched again when that guess was wrong). The rows of
+// one slot are tested together. On return e0/e1 hold the slot set with row f. With
+// `diag`, each row's record is written once: tested rows by their group's first lane (the
+// stop row with `stop_resid`), untested and bonus rows after the walk.
+__device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w, int b, const ReqHead& h,
+                                                 int lo_pre, int lane, int dt0, P1Part& e0, P1Part& e1,
+                                                 sv_row_diag* diag, float stop_resid) {
   ReqState q{};
-  q.lo = in.ro[b];
-  q.n = in.ro[b + 1] - q.lo;
-  q.T = in.temp[b];
-  q.tau = in.tau[b];
-  q.stop_slot = -1;
+  q.lo = h.lo;
+  q.n = h.n;
+  q.T = h.T;
+  q.tau = h.tau;
+  q.stop_half = 0;
+  q.stop_lane0 = 0;
   const bool req_ok = temperature_ok(q.T) && !__builtin_isnan(q.tau);
   q.c = req_ok ? fold_scale(q.T) : 0.0f;
   const int nw = in.w1;
-  const int per_group = (2 * kWave) / nw;
+  const int rows_half = kWave / nw;
+  const int per_group = 2 * rows_half;
   const int nd = q.n - 1;  // rows that carry a drafted token: all but the last
-
-  const int dt0 = in.dt[q.lo + min(lane, max(nd - 1, 0))];  // lane j: row j's drafted token (j < nd)
-  {
-    const int ne = min(per_group, max(nd, 1)) * nw;
-    const P1Part* base = w.part1 + (int64_t)q.lo * nw;
-    e0 = base[min(lane, ne - 1)];
-    e1 = base[min(lane + kWave, ne - 1)];
-  }
+  if (q.lo != lo_pre) prefetch_rows(in, w, q.lo, lane, dt0, e0, e1);  // requests of different lengths
   // Proposal rows: the rows before the first drafted token outside [0, V).
   q.n_prop = nd;
   for (int base = 0; base < nd; base += kWave) {
@@ -554,44 +598,49 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
     return q;
   }
   int k = q.n_prop;
-  for (int j0 = 0; j0 < q.n_prop; j0 += per_group) {
-    const int nrows = min(per_group, q.n_prop - j0);
+  bool stopped = false;
+  const int jj = lane / nw;  // the lane's row within a slot set
+  for (int j0 = 0; j0 < q.n_prop && !stopped; j0 += per_group) {
     if (j0 > 0) {  // windows longer than one group
-      const int ne = nrows * nw;
-      const P1Part* base = w.part1 + (int64_t)(q.lo + j0) * nw;
-      e0 = base[min(lane, ne - 1)];
-      e1 = base[min(lane + kWave, ne - 1)];
+      int unused;
+      prefetch_rows(in, w, q.lo + j0, lane, unused, e0, e1);
     }
-    bool stop = false;
-    for (int jj = 0; jj < nrows; ++jj) {
-      const int j = j0 + jj;
-      const bool m0 = lane / nw == jj;
-      const bool m1 = (lane + kWave) / nw == jj;
-      const int D = j < kWave ? __shfl(dt0, j) : in.dt[q.lo + j];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {  // unrolled: e0 and e1 stay in registers
+      const int jh = j0 + half * rows_half;
+      if (jh >= q.n_prop) break;
+      const int j = jh + jj;
+      const bool live = j < q.n_prop;
+      const int jc = min(j, nd - 1);
+      const int D = jc < kWave ? __shfl(dt0, jc) : in.dt[q.lo + jc];
       RowStat rs;
-      const RowEval ev = eval_row(in, e0, e1, m0, m1, b, j, D, q.T, q.tau, q.c, rs);
-      const bool accepted = ev.verdict == SV_ROW_ACCEPT;
-      if (diag != nullptr && lane == 0) {
+      const RowEval ev = eval_rows(in, pick_part(half != 0, e0, e1), live, nw, b, j, D, q.T, q.tau, q.c, rs);
+      const uint64_t m = __ballot(live && ev.verdict != SV_ROW_ACCEPT);
+      int stop_j = INT32_MAX;
+      if (m != 0) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        stop_j = jh + src / nw;
+        k = stop_j;
+        q.final_verdict = __shfl(ev.verdict, src);
+        q.stop = RowStat{__shfl(rs.m_t, src), __shfl(rs.mc_t, src), __shfl(rs.m_d, src), __shfl(rs.mc_d, src),
+                         __shfl(rs.s_t, src), __shfl(rs.s_d, src), __shfl(rs.am_t, src), __shfl(rs.am_d, src)};
+        q.stop_half = half;
+        q.stop_lane0 = (src / nw) * nw;
+        stopped = true;
+      }
+      if (diag != nullptr && live && (lane & (nw - 1)) == 0 && j <= stop_j) {
         sv_row_diag dg;
         dg.p_D = ev.p_D;
         dg.q_D = ev.q_D;
         dg.mu_D = ev.mu_D;
         dg.u = ev.u;
-        dg.resid_mass = accepted ? NAN : stop_resid;
+        dg.resid_mass = j == stop_j ? stop_resid : NAN;
         dg.verdict = ev.verdict;
         dg.pad0 = dg.pad1 = 0;
         diag[q.lo + j] = dg;
       }
-      if (!accepted) {
-        k = j;
-        q.final_verdict = ev.verdict;
-        q.stop = rs;
-        q.stop_slot = jj;
-        stop = true;
-        break;
-      }
+      if (stopped) break;
     }
-    if (stop) break;
   }
   q.k = k;
   q.f = q.lo + k;
@@ -613,6 +662,22 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
       }
     }
   }
+  // Keep the request in scalar registers.
+  q.n_prop = uni(q.n_prop);
+  q.k = uni(q.k);
+  q.f = uni(q.f);
+  q.kind = uni(q.kind);
+  q.final_verdict = uni(q.final_verdict);
+  q.stop.m_t = uni(q.stop.m_t);
+  q.stop.mc_t = uni(q.stop.mc_t);
+  q.stop.m_d = uni(q.stop.m_d);
+  q.stop.mc_d = uni(q.stop.mc_d);
+  q.stop.s_t = uni(q.stop.s_t);
+  q.stop.s_d = uni(q.stop.s_d);
+  q.stop.am_t = uni(q.stop.am_t);
+  q.stop.am_d = uni(q.stop.am_d);
+  q.stop_half = uni(q.stop_half);
+  q.stop_lane0 = uni(q.stop_lane0);
   return q;
 }
 
@@ -649,8 +714,10 @@ __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, co
     if (invalid) {
       for (int j = lane; j < q.n; j += kWave) out.diag[q.lo + j] = untested_diag();
     } else {
+      int dt0;
       P1Part e0, e1;
-      walk_request(in, w, b, lane, e0, e1, out.diag, resid);
+      prefetch_rows(in, w, q.lo, lane, dt0, e0, e1);
+      walk_request(in, w, b, request_head(in, b), q.lo, lane, dt0, e0, e1, out.diag, resid);
     }
   }
 }
@@ -700,8 +767,7 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
 
 // Wave gw of the grid serves span gw % w2 of request gw / w2.
 template <typename E, int VEC, int U>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void pass2_kernel(Inputs in, Work w,
-                                                                                             Outputs out) {
+__global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Outputs out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -710,7 +776,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int g = (int)(gw % in.w2);
   const bool head = g == 0;
 
-  if (!w.hdr->ro_valid) {
+  // One round trip brings the batch check, the request's head, and its rows' drafted
+  // tokens and partials at the first row the head would give if every request had the
+  // same length.
+  const int ro_valid = w.hdr->ro_valid;
+  const ReqHead rh = request_head(in, b);
+  const int lo_pre = (int)((int64_t)b * in.R / in.B);
+  int dt0;
+  P1Part e0, e1;
+  prefetch_rows(in, w, lo_pre, lane, dt0, e0, e1);
+  if (!ro_valid) {
     // Broken row_offsets: the whole batch fails closed. The head wave of request b
     // clears an even share of the rows.
     if (head) {
@@ -727,8 +802,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     return;
   }
 
-  P1Part e0, e1;
-  const ReqState q = walk_request(in, w, b, lane, e0, e1, nullptr, NAN);
+  const ReqState q = walk_request(in, w, b, rh, lo_pre, lane, dt0, e0, e1, nullptr, NAN);
   if (q.kind == kKindInvalid) {
     if (head) emit_request(in, w, out, b, q, true, -1, NAN, lane);
     return;
@@ -749,6 +823,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const uint32_t k0 = seed_lo(in.seed), k1 = seed_hi(in.seed);
   constexpr int step = U * kWave;
   constexpr int G = VEC >= 4 ? 4 : 1;  // logits sharing one Philox block
+  const int nsteps = (sp.end - sp.begin + step - 1) / step;
 
   P2Part part{};
   part.key = -INFINITY;
@@ -761,26 +836,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   if (q.kind == kKindResidual) {
     const float c = q.c, mct = q.stop.mc_t, mcd = q.stop.mc_d, tau = q.tau;
     const float ist = (float)(1.0 / q.stop.s_t), isd = (float)(1.0 / q.stop.s_d);
-    float rsum = 0.0f;
-    Top2 t = top2_empty();
+    // Gate in the logit domain: q_x >= tau needs l_d*c - mcd >= log2(tau * s_d). The margin
+    // keeps every token whose fp32 q could reach tau; for the others mu = 0 and r = p, so q
+    // is computed only where the gate can pass.
+    const float gate_l = tau > 0.0f ? (float)(((double)mcd + log2((double)tau * q.stop.s_d) - 1e-3) / (double)c)
+                                    : -INFINITY;
     // Pruning bound. Pass 1 left, per wave of row f, the vector that held that wave's
-    // target maximum; the partials of row f are in this wave's registers. The best race key
-    // among those tokens is a key some token really has, so the winner's key is at least
-    // that large. A token whose residual r has r / E_min below half of it cannot win and
-    // draws no random number. Only tokens with mu <= p/2 serve: there r = p - mu carries at
-    // most twice the fp32 error of p, so the bound is exact to about 1e-6 and the factor 2
-    // absorbs it.
-    const int nw1 = in.w1;
-    const int nh = nw1 * VEC;
-    int hx[VEC];
-    float hlt[VEC], hld[VEC];
+    // target maximum; row f's partials are in this wave's registers. The best race key
+    // among (up to 128 of) those tokens is a key some token really has, so the winner's key
+    // is at least that large. A token whose residual r has r / E_min below half of it cannot
+    // win and draws no random number. Only tokens with mu <= p/2 serve: there r = p - mu
+    // carries at most twice the fp32 error of p, and the factor 2 absorbs all fp32 error.
+    const int nh = in.w1 * VEC;
+    const int hsrc = q.stop_half ? e1.am_t : e0.am_t;
+    int hx[2];
+    float hlt[2], hld[2];
 #pragma unroll
-    for (int s = 0; s < VEC; ++s) {
+    for (int s = 0; s < 2; ++s) {
       const int ti = lane + s * kWave;
-      const int pos = q.stop_slot * nw1 + min(ti / VEC, nw1 - 1);
-      const int h0 = __shfl(e0.am_t, pos & (kWave - 1));
-      const int h1 = __shfl(e1.am_t, pos & (kWave - 1));
-      const int hv = pos < kWave ? h0 : h1;
+      const int hv = __shfl(hsrc, q.stop_lane0 + min(ti / VEC, in.w1 - 1));
       int x = (ti < nh && hv >= 0) ? hv * VEC + ti % VEC : -1;
       x = x < in.V ? x : -1;
       hx[s] = x;
@@ -788,67 +862,81 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       hlt[s] = to_float(trow[xc]);
       hld[s] = to_float(drow[xc]);
     }
-    // The span's first batch is requested before the hint logits are used, so both
-    // arrive in one round trip.
-    CH ta[U], da[U];
-    if (sp.begin < sp.end) {
+    // The span's first batch is requested before the hint logits are used.
+    CH ta[U], da[U], tb[U], db[U];
+    if (nsteps > 0) {
       load_chunks<false>(ta, trow, sp.begin, lane, sp.end);
       load_chunks<false>(da, drow, sp.begin, lane, sp.end);
     }
     float kh = 0.0f;
 #pragma unroll
-    for (int s = 0; s < VEC; ++s) {
+    for (int s = 0; s < 2; ++s) {
       const float p = fast_exp2(fmaf(hlt[s], c, -mct)) * ist;
       const float qq = fast_exp2(fmaf(hld[s], c, -mcd)) * isd;
       const float mu = qq >= tau ? qq : 0.0f;
       if (hx[s] >= 0 && p > 0.0f && mu <= 0.5f * p)
-        kh = fmaxf(kh, (float)((double)(p - mu) / expo64(race_word(in.seed, hx[s], q.k, b))));
+        kh = fmaxf(kh, (p - mu) / expo32(race_word(in.seed, hx[s], q.k, b)));
     }
     kh = wave_max(kh);
     const float pthr = kh * (float)(kEminLow * 0.5);
+
+    float rsum = 0.0f;
+    Top2 t = top2_empty();
     auto fold_res = [&](const CH (&xt)[U], const CH (&xd)[U], int v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int x0 = (v0 + u * kWave) * VEC;
+        float rv[VEC];
+        bool gated = false;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          rv[e] = fast_exp2(fmaf(xt[u].get(e), c, -mct)) * ist;  // p; r = p where mu = 0
+          gated |= xd[u].get(e) >= gate_l;
+        }
+        if (gated) {  // rare: a token of this vector may pass the gate
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float qq = fast_exp2(fmaf(xd[u].get(e), c, -mcd)) * isd;
+            const float mu = qq >= tau ? qq : 0.0f;
+            rv[e] = fmaxf(rv[e] - mu, 0.0f);
+          }
+        }
 #pragma unroll
         for (int gg = 0; gg < VEC; gg += G) {
-          float rv[G];
           bool any = false;
 #pragma unroll
           for (int e = 0; e < G; ++e) {
-            const float p = fast_exp2(fmaf(xt[u].get(gg + e), c, -mct)) * ist;
-            const float qq = fast_exp2(fmaf(xd[u].get(gg + e), c, -mcd)) * isd;
-            const float mu = qq >= tau ? qq : 0.0f;
-            const float r = fmaxf(p - mu, 0.0f);
-            rsum += r;
-            rv[e] = r;
-            any |= (r > 0.0f && r >= pthr);
+            rsum += rv[gg + e];
+            any |= (rv[gg + e] > 0.0f && rv[gg + e] >= pthr);
           }
           if (any) {
             const int xg = x0 + gg;
             const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
 #pragma unroll
             for (int e = 0; e < G; ++e) {
-              if (rv[e] > 0.0f && rv[e] >= pthr) {
+              const float r = rv[gg + e];
+              if (r > 0.0f && r >= pthr) {
                 const int x = xg + e;
                 const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
-                top2_push(t, rv[e] / expo32(wd), x, xt[u].get(gg + e), xd[u].get(gg + e));
+                top2_push(t, r / expo32(wd), x, xt[u].get(gg + e), xd[u].get(gg + e));
               }
             }
           }
         }
       }
     };
-    // One batch per step; at the planned split a wave's span is about one batch.
-    const int nsteps = (sp.end - sp.begin + step - 1) / step;
-    for (int i = 0, base = sp.begin; i < nsteps; ++i, base += step) {
+    // Double buffering with an exit only at the bottom (see pass 1).
+    for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+      load_chunks<false>(tb, trow, base + step, lane, sp.end);
+      load_chunks<false>(db, drow, base + step, lane, sp.end);
       mask_chunks(ta, base, lane, sp.end);
       mask_chunks(da, base, lane, sp.end);
       fold_res(ta, da, base + lane);
-      if (i + 1 < nsteps) {
-        load_chunks<false>(ta, trow, base + step, lane, sp.end);
-        load_chunks<false>(da, drow, base + step, lane, sp.end);
-      }
+      load_chunks<false>(ta, trow, base + 2 * step, lane, sp.end);
+      load_chunks<false>(da, drow, base + 2 * step, lane, sp.end);
+      mask_chunks(tb, base + step, lane, sp.end);
+      mask_chunks(db, base + step, lane, sp.end);
+      fold_res(tb, db, base + step + lane);
     }
     wave_top2(t);
     part.rsum = wave_sum(rsum);
@@ -873,33 +961,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     Acc a = acc_empty();
     int bad = 0;
     Top2 t = top2_empty();
-    float wbest = -INFINITY;  // best log2 key the wave has seen so far
-    CH ta[U];
+    float wbest = -INFINITY;  // best log2 key the wave has drawn so far
+    CH ta[U], tb[U];
     auto fold_bonus = [&](const CH (&xt)[U], int v0) __attribute__((always_inline)) {
       if (race) fold_max<false>(a, xt, v0, bad);  // max and NaN / +inf check
       else fold_max<true>(a, xt, v0, bad);       // ... and the lowest index of the max
       if (race) {
+        // A token's log2 key is l*c - log2(E) with 2^-24 < E < 16.7, so it lies within
+        // (l*c - 4.06, l*c + 24). The wave's largest l*c so far therefore gives a key of at
+        // least max(l*c) - 4.06, and a token more than 28.1 below that cannot win. The
+        // margins (4.1, 25) absorb fp32 error.
+        const float lb = fmaxf(wbest, wave_max(a.m) * c - 4.1f);
         float lbest = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int x0 = (v0 + u * kWave) * VEC;
 #pragma unroll
           for (int gg = 0; gg < VEC; gg += G) {
-            // A token's log2 key is l*c - log2(E) <= l*c + 24 (E >= 2^-24). It cannot win if
-            // that bound is a factor 2 below a key already seen.
             float av[G];
             bool any = false;
 #pragma unroll
             for (int e = 0; e < G; ++e) {
               av[e] = xt[u].get(gg + e) * c;
-              any |= av[e] + 25.0f >= wbest;
+              any |= av[e] + 25.0f >= lb;
             }
             if (any) {
               const int xg = x0 + gg;
               const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
 #pragma unroll
               for (int e = 0; e < G; ++e) {
-                if (av[e] + 25.0f >= wbest) {
+                if (av[e] + 25.0f >= lb) {
                   const int x = xg + e;
                   const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
                   const float key = av[e] - __log2f(expo32(wd));
@@ -913,12 +1004,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         wbest = fmaxf(wbest, wave_max(lbest));
       }
     };
-    if (sp.begin < sp.end) load_chunks<false>(ta, trow, sp.begin, lane, sp.end);
-    const int nsteps = (sp.end - sp.begin + step - 1) / step;
-    for (int i = 0, base = sp.begin; i < nsteps; ++i, base += step) {
+    if (nsteps > 0) load_chunks<false>(ta, trow, sp.begin, lane, sp.end);
+    for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+      load_chunks<false>(tb, trow, base + step, lane, sp.end);
       mask_chunks(ta, base, lane, sp.end);
       fold_bonus(ta, base + lane);
-      if (i + 1 < nsteps) load_chunks<false>(ta, trow, base + step, lane, sp.end);
+      load_chunks<false>(ta, trow, base + 2 * step, lane, sp.end);
+      mask_chunks(tb, base + step, lane, sp.end);
+      fold_bonus(tb, base + step + lane);
     }
     float m;
     float unused;
@@ -1043,8 +1136,9 @@ static hipError_t counters_ready(const Plan& p, char* ws, hipStream_t stream) {
   return hipSuccess;
 }
 
-// Resident waves per kernel on a device: compute units times the workgroups of the kernel
-// that fit on one, times four waves. Queried once per (device, kernel).
+// Waves a streaming kernel should run on a device: kTargetWavesPerCU per compute unit, or
+// fewer if fewer fit (compute units times the kernel's workgroups per unit times four
+// waves). Queried once per (device, kernel).
 struct SlotsSeen {
   int device;
   const void* fn;
@@ -1068,7 +1162,8 @@ static hipError_t resident_waves(const void* fn, int64_t* slots) {
   int cus = 0, per_cu = 0;
   if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
   if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0)) != hipSuccess) return err;
-  const int64_t s = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1) * kWavesPerBlock;
+  const int64_t fit = (int64_t)(per_cu > 0 ? per_cu : 1) * kWavesPerBlock;
+  const int64_t s = (int64_t)(cus > 0 ? cus : 1) * (fit < kTargetWavesPerCU ? fit : kTargetWavesPerCU);
   if (g_slots_n < 64) g_slots[g_slots_n++] = SlotsSeen{dev, fn, s};
   *slots = s;
   return hipSuccess;
@@ -1077,8 +1172,8 @@ static hipError_t resident_waves(const void* fn, int64_t* slots) {
 template <typename E, int VEC>
 hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& out, hipStream_t stream,
                        hipEvent_t const* ev) {
-  constexpr int U1 = VEC == 1 ? 12 : 3;  // pass 1: 12 logits per lane per array and step (x2 buffers)
-  constexpr int U2 = VEC == 1 ? 16 : 6;  // pass 2: one larger batch per array and step
+  constexpr int U1 = VEC == 1 ? 8 : 2;  // pass 1: chunks per lane per array and step (x2 buffers)
+  constexpr int U2 = VEC == 1 ? 8 : 2;  // pass 2: the same
   const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
   const void* k2 = reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2>);
   int64_t slots1 = 0, slots2 = 0;

@@ -111,17 +111,17 @@ int main() {
   int32_t dummy[4];
   const void* v = dummy;
   CHECK(make_plan(sv_shape{64, 320, 151936, SV_BF16}, &p) == SV_OK);
-  CHECK(p.w1max == 49 && p.w2max == 50 && p.total % 256 == 0 && p.off_ticket2 < p.total);
+  CHECK(p.w1max == 64 && p.w2max == 64 && p.total % 256 == 0 && p.off_ticket2 < p.total);
   {
-    const Launch l = pick_waves(p, 4096, 3072);
-    CHECK(l.w1 == 16 && l.w2 == 48 && l.blocks1 == 320 * 16 / 4 && l.blocks2 == 64 * 48 / 4);
+    const Launch l = pick_waves(p, 1536, 1536);  // six waves per CU on 256 CUs
+    CHECK(l.w1 == 4 && l.w2 == 24 && l.blocks1 == 256 * 4 / 4 && l.blocks2 == 64 * 24 / 4);
     const Launch m = pick_waves(p, 1, 1);
-    CHECK(m.w1 == 1 && m.w2 == 1 && m.blocks1 == 80 && m.blocks2 == 16);
+    CHECK(m.w1 == 1 && m.w2 == 1 && m.blocks1 == 64 && m.blocks2 == 16);
     const Launch h = pick_waves(p, 1 << 30, 1 << 30);
-    CHECK(h.w1 == p.w1max && h.w2 == p.w2max);
+    CHECK(h.w1 == 64 && h.w2 == p.w2max);
   }
   CHECK(make_plan(sv_shape{1, 1, 1, SV_F32}, &p) == SV_OK && p.w1max == 1 && p.w2max == 1);
-  CHECK(pick_waves(p, 4096, 4096).w1 == 1 && pick_waves(p, 4096, 4096).blocks1 == 1);
+  CHECK(pick_waves(p, 4096, 4096).w1 == 1 && pick_waves(p, 4096, 4096).blocks1 == 1);  // no row to stream
   CHECK(make_plan(sv_shape{0, 0, 7, SV_F32}, &p) == SV_OK);
   CHECK(make_plan(sv_shape{3, 2, 7, SV_F32}, &p) == SV_E_SHAPE);
   CHECK(make_plan(sv_shape{3, 4, 7, 5}, &p) == SV_E_DTYPE);
@@ -132,7 +132,9 @@ int main() {
       CHECK(make_plan(sv_shape{B, 5 * B, V, SV_BF16}, &p) == SV_OK);
       CHECK(sv_workspace_bytes(sv_shape{B, 5 * B, V, SV_BF16}) == p.total);
       CHECK(p.w1max >= 1 && p.w2max >= 1 && p.w1max <= 64 && p.w2max <= 64);
-      CHECK(p.w1max == 1 || (long long)p.w1max * 2 * kBatchBytes1 <= (long long)V * 2);
+      CHECK(p.w1max == 1 || (long long)p.w1max * 2 * kBatchBytes <= (long long)V * 2);
+      const Launch l = pick_waves(p, 4096, 3072);
+      CHECK((l.w1 & (l.w1 - 1)) == 0 && l.w1 <= p.w1max && l.w2 <= p.w2max && l.blocks1 >= 1);
     }
   const sv_shape ok{2, 4, 5, SV_F32};
   CHECK(check_call(ok, v, v, dummy, dummy, (const float*)v, (const float*)v, dummy, dummy, v, 1 << 20, &p) == SV_OK);

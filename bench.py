@@ -35,6 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_traffic_gated_B64_T4_V15193
 KERNEL_SOURCES = [os.path.join(ROOT, "lossless_rejection_sampling_row_amd", "csrc", f)
                   for f in ("sv_kernels.hip", "sv_device.h", "sv_plan.h")]
 DEFAULT_SETS = {1: 2, 2: 8, 3: 4, 4: 2, 5: 2}
+COPY_MIB = 384  # calibration copy: larger than the 256 MB Infinity Cache
 
 
 def log(*a):
@@ -100,6 +101,63 @@ def cpu_baseline(w, budget_s: float):
                       f"{rows} rows in {el:.1f} s, one process (numpy, single-threaded)"}
 
 
+def _counter_means(path, counter):
+    """Mean counter value per dispatch, per kernel name, from a rocprofv3 counter_collection.csv."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per pass-1 launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    the same counter on the calibration copy: its largest dispatch moved COPY_MIB MiB each way."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for k, vs in d.items() if key(k) for v in vs]
+        return vals
+
+    p1f = pick(fetch, lambda k: "pass1_kernel" in k)
+    p1w = pick(write, lambda k: "pass1_kernel" in k)
+    cf = max(pick(fetch, lambda k: "copyBuffer" in k or "copy" in k.lower()))
+    cw = max(pick(write, lambda k: "copyBuffer" in k or "copy" in k.lower()))
+    copy_bytes = COPY_MIB * 1024 * 1024
+    f_fetch = copy_bytes / (cf * 1024.0)
+    f_write = copy_bytes / (cw * 1024.0)
+    fetch_kib = sum(p1f) / len(p1f)
+    write_kib = sum(p1w) / len(p1w)
+    rec = {
+        "kernel": "pass1_kernel",
+        "workload": "gated B=64 T=4 V=151936 bf16",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(fetch_kib, 1),
+        "write_kib_per_dispatch": round(write_kib, 1),
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cf,
+        "copy_write_kib": cw,
+        "fetch_scale": round(f_fetch, 4),
+        "write_scale": round(f_write, 4),
+        "hbm_bytes_per_launch": int(fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o f -- python3 bench.py --steps 8 --warmup 2 "
+            f"--cpu-budget 0 --copy-calibration {COPY_MIB}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o w -- python3 bench.py --steps 8 --warmup 2 "
+            f"--cpu-budget 0 --copy-calibration {COPY_MIB}",
+            "python3 bench.py --write-traffic <dir>/f_counter_collection.csv <dir>/w_counter_collection.csv",
+        ],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +166,16 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--sets", type=int, default=None, help="distinct input sets rotated through")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the steps, copy a MIB-MiB device buffer three times (a plain copy of known size "
+                         "whose FETCH_SIZE / WRITE_SIZE scale the counters of the verify kernels)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE runs "
+                         "with --copy-calibration) into the traffic record the roofline entry reads")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this verify "
@@ -219,6 +286,15 @@ def main():
                 "frac": round(p1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "pass1_kernel", "launch_us": round(float(p1_ms.mean()) * 1e3, 2),
                 "alg_bytes_per_launch": int(p1_bytes.mean())}
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_budget > 0:

@@ -1136,9 +1136,9 @@ static hipError_t counters_ready(const Plan& p, char* ws, hipStream_t stream) {
   return hipSuccess;
 }
 
-// Waves a streaming kernel should run on a device: kTargetWavesPerCU per compute unit, or
-// fewer if fewer fit (compute units times the kernel's workgroups per unit times four
-// waves). Queried once per (device, kernel).
+// Waves a kernel should run on a device: the target per compute unit, or fewer if fewer
+// fit (compute units times the kernel's workgroups per unit times four waves). Queried
+// once per (device, kernel).
 struct SlotsSeen {
   int device;
   const void* fn;
@@ -1149,7 +1149,7 @@ static std::mutex g_slots_mu;
 static SlotsSeen g_slots[64];
 static int g_slots_n = 0;
 
-static hipError_t resident_waves(const void* fn, int64_t* slots) {
+static hipError_t resident_waves(const void* fn, int per_cu_target, int64_t* slots) {
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
@@ -1163,7 +1163,7 @@ static hipError_t resident_waves(const void* fn, int64_t* slots) {
   if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
   if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0)) != hipSuccess) return err;
   const int64_t fit = (int64_t)(per_cu > 0 ? per_cu : 1) * kWavesPerBlock;
-  const int64_t s = (int64_t)(cus > 0 ? cus : 1) * (fit < kTargetWavesPerCU ? fit : kTargetWavesPerCU);
+  const int64_t s = (int64_t)(cus > 0 ? cus : 1) * (fit < per_cu_target ? fit : per_cu_target);
   if (g_slots_n < 64) g_slots[g_slots_n++] = SlotsSeen{dev, fn, s};
   *slots = s;
   return hipSuccess;
@@ -1177,9 +1177,9 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
   const void* k2 = reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2>);
   int64_t slots1 = 0, slots2 = 0;
-  hipError_t err = resident_waves(k1, &slots1);
+  hipError_t err = resident_waves(k1, kTargetWavesPerCU, &slots1);
   if (err != hipSuccess) return err;
-  if ((err = resident_waves(k2, &slots2)) != hipSuccess) return err;
+  if ((err = resident_waves(k2, kTargetWavesPerCU2, &slots2)) != hipSuccess) return err;
   const Launch l = pick_waves(p, slots1, slots2);
   in.w1 = l.w1;
   in.w2 = l.w2;

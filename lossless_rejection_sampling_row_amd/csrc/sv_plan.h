@@ -26,6 +26,10 @@ constexpr int kBatchBytes = 2 * kWave * 16;
 // contiguous spans with small batches, read HBM faster than a full-occupancy grid of
 // shorter spans (29.5 us against 33 us for pass 1).
 constexpr int kTargetWavesPerCU = 6;
+// Pass 2 draws from one row per request. Its waves are latency-bound, so it runs more of
+// them: with 12 per CU, the gated batch above draws in 36 us, against 45 us with 6 per CU
+// and 42 us with 16 per CU.
+constexpr int kTargetWavesPerCU2 = 12;
 
 // Row verdict used inside the kernels besides the public SV_ROW_* codes.
 enum : int32_t { kRowInvalid = 5 };

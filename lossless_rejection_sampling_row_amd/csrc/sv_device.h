@@ -79,12 +79,18 @@ __device__ __forceinline__ float uniform_open(uint32_t w) {
   return (float)((w >> 9) * 2u + 1u) * 0x1p-24f;
 }
 
-// fp32 race exponential for candidate selection. It is accurate enough to rank
-// keys inside a slice; the final choice is re-evaluated in fp64. The guard
-// keeps it strictly positive.
+// fp32 race exponential E = -ln(U) for ranking candidates; the final choice is
+// re-evaluated in fp64. The guard keeps it strictly positive.
 __device__ __forceinline__ float expo32(uint32_t w) {
   const float e = -__logf(uniform_open(w));
   return fmaxf(e, 1e-30f);
+}
+
+// An upper bound on E = -ln(U), for lower bounds on race keys that prune tokens. A
+// relative 1e-3 and an absolute 1e-6 cover the fast logarithm's error, also for U next to
+// 1 where E is about 6e-8 and the logarithm's relative accuracy is poor.
+__device__ __forceinline__ float expo32_upper(uint32_t w) {
+  return fmaf(-__logf(uniform_open(w)), 1.001f, 1e-6f);
 }
 
 __device__ __forceinline__ double expo64(uint32_t w) { return -log((double)uniform_open(w)); }

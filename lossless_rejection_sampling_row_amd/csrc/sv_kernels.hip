@@ -722,6 +722,13 @@ __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, co
   }
 }
 
+// How far below the wave's best fp32 race key a candidate is still re-evaluated exactly:
+// a relative 1e-3 for ratio keys r/E, 0.01 in log2 units for log keys. Both are far above
+// the keys' fp32 error outside decision-boundary requests.
+constexpr float kRatioKeySlack = 1e-3f;
+constexpr float kKeyErr = 1e-5f;
+constexpr float kLogKeySlack = 0.01f;
+
 // fp64 race key of token x on a residual row, from its two logits.
 __device__ __forceinline__ double residual_key64(double lt, double ld, double c, double mct, double mcd,
                                                  double st, double sd, double tau, uint32_t word) {
@@ -739,6 +746,28 @@ __device__ __forceinline__ double p_logkey64(double l, double T, uint32_t word) 
   return l / T - log(expo64(word));
 }
 
+// The race winner among the lanes' fp32 top-2 candidates. Every candidate whose fp32 key
+// reaches `cut` is re-evaluated exactly by `eval(index, a, b)`; the best exact key wins,
+// ties to the lower index. With `cut` a safe margin below the wave's best fp32 key, no
+// candidate that could win exactly is left out.
+template <class F>
+__device__ __forceinline__ void resolve_race(const Top2& t, float cut, F eval, double& bk, int& bi) {
+  bk = -INFINITY;
+  bi = INT32_MAX;
+  if (t.i1 != INT32_MAX && t.k1 >= cut) {
+    bk = eval(t.i1, t.a1, t.b1);
+    bi = t.i1;
+  }
+  if (t.i2 != INT32_MAX && t.k2 >= cut) {
+    const double k2 = eval(t.i2, t.a2, t.b2);
+    if (beats(k2, t.i2, bk, bi)) {
+      bk = k2;
+      bi = t.i2;
+    }
+  }
+  wave_best(bk, bi);
+}
+
 // A race over p read by one wave: the rare fallback for a residual with no mass.
 __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState& q, int b, int lane) {
   Top2 t = top2_empty();
@@ -750,18 +779,11 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
       top2_push(t, a - __log2f(expo32(wd)), (int)x, l, 0.0f);
     }
   }
-  wave_top2(t);
-  double bk = -INFINITY;
-  int bi = INT32_MAX;
-  if (lane < 2) {
-    const int x = lane == 0 ? t.i1 : t.i2;
-    const float l = lane == 0 ? t.a1 : t.a2;
-    if (x != INT32_MAX) {
-      bk = p_logkey64((double)l, (double)q.T, race_word(in.seed, x, q.k, b));
-      bi = x;
-    }
-  }
-  wave_best(bk, bi);
+  double bk;
+  int bi;
+  resolve_race(t, wave_max(t.k1) - kLogKeySlack,
+               [&](int x, float l, float) { return p_logkey64((double)l, (double)q.T, race_word(in.seed, x, q.k, b)); },
+               bk, bi);
   return bi;
 }
 
@@ -842,11 +864,11 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     const float gate_l = tau > 0.0f ? (float)(((double)mcd + log2((double)tau * q.stop.s_d) - 1e-3) / (double)c)
                                     : -INFINITY;
     // Pruning bound. Pass 1 left, per wave of row f, the vector that held that wave's
-    // target maximum; row f's partials are in this wave's registers. The best race key
-    // among (up to 128 of) those tokens is a key some token really has, so the winner's key
-    // is at least that large. A token whose residual r has r / E_min below half of it cannot
-    // win and draws no random number. Only tokens with mu <= p/2 serve: there r = p - mu
-    // carries at most twice the fp32 error of p, and the factor 2 absorbs all fp32 error.
+    // target maximum; row f's partials are in this wave's registers. A lower bound on the
+    // race key of (up to 128 of) those tokens bounds the winner's key from below. A token
+    // whose residual r has r / E_min below half of it cannot win and draws no random number.
+    // As the wave draws, the same lower bound on its own candidates' keys raises the bar.
+    // The bounds shave kKeyErr off every fp32 factor, more than its rounding error.
     const int nh = in.w1 * VEC;
     const int hsrc = q.stop_half ? e1.am_t : e0.am_t;
     int hx[2];
@@ -874,11 +896,13 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       const float p = fast_exp2(fmaf(hlt[s], c, -mct)) * ist;
       const float qq = fast_exp2(fmaf(hld[s], c, -mcd)) * isd;
       const float mu = qq >= tau ? qq : 0.0f;
-      if (hx[s] >= 0 && p > 0.0f && mu <= 0.5f * p)
-        kh = fmaxf(kh, (p - mu) / expo32(race_word(in.seed, hx[s], q.k, b)));
+      const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
+      if (hx[s] >= 0 && rl > 0.0f)
+        kh = fmaxf(kh, rl / expo32_upper(race_word(in.seed, hx[s], q.k, b)) * (1.0f - kKeyErr));
     }
     kh = wave_max(kh);
-    const float pthr = kh * (float)(kEminLow * 0.5);
+    float pthr = kh * (float)(kEminLow * 0.5);
+    float safe = 0.0f;  // lane's best lower bound on a drawn key
 
     float rsum = 0.0f;
     Top2 t = top2_empty();
@@ -886,19 +910,19 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int x0 = (v0 + u * kWave) * VEC;
-        float rv[VEC];
+        float rv[VEC], mv[VEC];
         bool gated = false;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           rv[e] = fast_exp2(fmaf(xt[u].get(e), c, -mct)) * ist;  // p; r = p where mu = 0
+          mv[e] = 0.0f;
           gated |= xd[u].get(e) >= gate_l;
         }
         if (gated) {  // rare: a token of this vector may pass the gate
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             const float qq = fast_exp2(fmaf(xd[u].get(e), c, -mcd)) * isd;
-            const float mu = qq >= tau ? qq : 0.0f;
-            rv[e] = fmaxf(rv[e] - mu, 0.0f);
+            mv[e] = qq >= tau ? qq : 0.0f;
           }
         }
 #pragma unroll
@@ -906,6 +930,9 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
           bool any = false;
 #pragma unroll
           for (int e = 0; e < G; ++e) {
+            const float p = rv[gg + e], mu = mv[gg + e];
+            rv[gg + e] = fmaxf(p - mu, 0.0f);
+            mv[gg + e] = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
             rsum += rv[gg + e];
             any |= (rv[gg + e] > 0.0f && rv[gg + e] >= pthr);
           }
@@ -919,6 +946,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
                 const int x = xg + e;
                 const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
                 top2_push(t, r / expo32(wd), x, xt[u].get(gg + e), xd[u].get(gg + e));
+                safe = fmaxf(safe, mv[gg + e] / expo32_upper(wd) * (1.0f - kKeyErr));
               }
             }
           }
@@ -937,21 +965,17 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       mask_chunks(tb, base + step, lane, sp.end);
       mask_chunks(db, base + step, lane, sp.end);
       fold_res(tb, db, base + step + lane);
+      pthr = fmaxf(pthr, wave_max(safe) * (float)(kEminLow * 0.5));
     }
-    wave_top2(t);
     part.rsum = wave_sum(rsum);
-    double bk = -INFINITY;
-    int bi = INT32_MAX;
-    if (lane < 2) {
-      const int x = lane == 0 ? t.i1 : t.i2;
-      if (x != INT32_MAX) {
-        bk = residual_key64((double)(lane == 0 ? t.a1 : t.a2), (double)(lane == 0 ? t.b1 : t.b2), (double)c,
-                            (double)mct, (double)mcd, q.stop.s_t, q.stop.s_d, (double)tau,
-                            race_word(in.seed, x, q.k, b));
-        bi = x;
-      }
-    }
-    wave_best(bk, bi);
+    double bk;
+    int bi;
+    resolve_race(t, wave_max(t.k1) * (1.0f - kRatioKeySlack),
+                 [&](int x, float lt, float ld) {
+                   return residual_key64((double)lt, (double)ld, (double)c, (double)mct, (double)mcd, q.stop.s_t,
+                                         q.stop.s_d, (double)tau, race_word(in.seed, x, q.k, b));
+                 },
+                 bk, bi);
     part.key = bk;
     part.idx = bi == INT32_MAX ? -1 : bi;
   } else {
@@ -1021,17 +1045,13 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     part.gidx = race ? -1 : exact_argmax<CH>(trow, a, m);
     part.bad = wave_or(bad);
     if (race) {
-      wave_top2(t);
-      double bk = -INFINITY;
-      int bi = INT32_MAX;
-      if (lane < 2) {
-        const int x = lane == 0 ? t.i1 : t.i2;
-        if (x != INT32_MAX) {
-          bk = p_logkey64((double)(lane == 0 ? t.a1 : t.a2), (double)q.T, race_word(in.seed, x, q.k, b));
-          bi = x;
-        }
-      }
-      wave_best(bk, bi);
+      double bk;
+      int bi;
+      resolve_race(t, wave_max(t.k1) - kLogKeySlack,
+                   [&](int x, float l, float) {
+                     return p_logkey64((double)l, (double)q.T, race_word(in.seed, x, q.k, b));
+                   },
+                   bk, bi);
       part.key = bk;
       part.idx = bi == INT32_MAX ? -1 : bi;
     }

@@ -33,15 +33,20 @@ def _gpu():
 
 
 def _parity(batch, seeds=(None,), requests=None, label=""):
+    """Both entry points against the oracle: the diagnostic call (with row records, a kernel
+    of its own) and the plain call."""
     tot = Parity()
     g = upload(batch)
     for s in seeds:
         say(f"[parity] {label} seed={s if s is not None else batch['seed']}")
         gpu = run_gpu(batch, seed=s, gpu=g)
+        fast = run_gpu(batch, seed=s, gpu=g, diag=False)
         ora = run_oracle(batch, seed=s, requests=requests)
         tot.add(compare(batch, gpu, ora, requests=requests))
+        compare(batch, fast, ora, requests=requests, check_diag=False)
         if requests is not None:
             check_properties(batch, gpu)
+            check_properties(batch, fast)
     say(f"[parity] {label}: {tot}")
     return tot
 
@@ -88,6 +93,10 @@ def test_determinism_and_seed_dependence():
         assert np.array_equal(a.resid_mass.view(np.int64), b.resid_mass.view(np.int64))
     c = run_gpu(batch, seed=12, gpu=g)
     assert not np.array_equal(a.out_tokens, c.out_tokens)
+    for _ in range(3):  # the plain call: same tokens, run after run
+        f = run_gpu(batch, seed=11, gpu=g, diag=False)
+        assert np.array_equal(a.out_tokens, f.out_tokens)
+        assert np.array_equal(a.out_accept_len, f.out_accept_len)
 
 
 def test_stats_counters():
@@ -119,6 +128,7 @@ def _both(batch, label):
     gpu = run_gpu(batch)
     ora = run_oracle(batch)
     compare(batch, gpu, ora)
+    compare(batch, run_gpu(batch, diag=False), ora, check_diag=False)
     return gpu, ora
 
 

@@ -202,65 +202,98 @@ __device__ __forceinline__ float logit_at(const void* base, int dtype, int64_t i
 }
 
 // ------------------------------------------------------------------ wave64 reductions
-// Butterfly reductions: every lane ends with the same, order-fixed result.
+// Every lane ends with the same, order-fixed result. Inside a 16-lane row the lanes
+// exchange values by DPP (quad permutations, then the half-row and row mirrors), which
+// the VALU does without the LDS round trip of a shuffle. Each exchange pairs lanes by an
+// involution, so the two lanes of a pair combine the same two values and agree. The four
+// row results then combine in a fixed order from lanes 0, 16, 32 and 48.
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+enum : int {
+  kDppQuadXor1 = 0xB1,        // quad_perm [1,0,3,2]: lane i reads lane i ^ 1
+  kDppQuadXor2 = 0x4E,        // quad_perm [2,3,0,1]: lane i reads lane i ^ 2
+  kDppRowHalfMirror = 0x141,  // lane i of each 8-lane half row reads lane 7 - i
+  kDppRowMirror = 0x140       // lane i of each 16-lane row reads lane 15 - i
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ int lane_of(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_of(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double lane_of(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Combine within aligned groups of `width` lanes, width a power of two up to 16.
+template <class T, class Op>
+__device__ __forceinline__ T row_reduce(T x, Op op, int width) {
+  if (width > 1) x = op(x, dpp<kDppQuadXor1>(x));
+  if (width > 2) x = op(x, dpp<kDppQuadXor2>(x));
+  if (width > 4) x = op(x, dpp<kDppRowHalfMirror>(x));
+  if (width > 8) x = op(x, dpp<kDppRowMirror>(x));
   return x;
 }
 
-__device__ __forceinline__ double wave_max(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  x = row_reduce(x, op, 16);
+  return op(op(lane_of(x, 0), lane_of(x, 16)), op(lane_of(x, 32), lane_of(x, 48)));
+}
+
+// Groups of 32 or 64 lanes finish with shuffles between rows.
+template <class T, class Op>
+__device__ __forceinline__ T seg_reduce(T x, Op op, int width) {
+  x = row_reduce(x, op, width < 16 ? width : 16);
+  for (int o = 16; o < width; o <<= 1) x = op(x, __shfl_xor(x, o));
   return x;
 }
 
-__device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
-}
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+  __device__ __forceinline__ double operator()(double a, double b) const { return fmax(a, b); }
+};
+struct OpMin {
+  __device__ __forceinline__ int operator()(int a, int b) const { return min(a, b); }
+};
+struct OpOr {
+  __device__ __forceinline__ int operator()(int a, int b) const { return a | b; }
+};
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+  __device__ __forceinline__ double operator()(double a, double b) const { return a + b; }
+};
 
-__device__ __forceinline__ int wave_or(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x |= __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float wave_max(float x) { return wave_reduce(x, OpMax{}); }
+__device__ __forceinline__ double wave_max(double x) { return wave_reduce(x, OpMax{}); }
+__device__ __forceinline__ int wave_min(int x) { return wave_reduce(x, OpMin{}); }
+__device__ __forceinline__ int wave_or(int x) { return wave_reduce(x, OpOr{}); }
+__device__ __forceinline__ float wave_sum(float x) { return wave_reduce(x, OpSum{}); }
+__device__ __forceinline__ double wave_sum(double x) { return wave_reduce(x, OpSum{}); }
 
 // Reductions over aligned groups of `width` lanes (a power of two, at most 64): every lane
 // ends with its group's result, combined in a fixed order.
-__device__ __forceinline__ float seg_max(float x, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float seg_sum(float x, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ double seg_sum(double x, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ int seg_min(int x, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
-}
+__device__ __forceinline__ float seg_max(float x, int width) { return seg_reduce(x, OpMax{}, width); }
+__device__ __forceinline__ float seg_sum(float x, int width) { return seg_reduce(x, OpSum{}, width); }
+__device__ __forceinline__ double seg_sum(double x, int width) { return seg_reduce(x, OpSum{}, width); }
+__device__ __forceinline__ int seg_min(int x, int width) { return seg_reduce(x, OpMin{}, width); }
 
 // A value every lane of the wave holds alike, moved to a scalar register.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -279,16 +312,36 @@ __device__ __forceinline__ bool beats(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// The best (key, index) of the wave on every lane. "beats" is a strict order on pairs,
+// so the winner does not depend on the order of the exchanges.
+template <int CTRL>
+__device__ __forceinline__ void best_step(double& k, int& i) {
+  const double ko = dpp<CTRL>(k);
+  const int io = dpp<CTRL>(i);
+  if (beats(ko, io, k, i)) {
+    k = ko;
+    i = io;
+  }
+}
+
 __device__ __forceinline__ void wave_best(double& k, int& i) {
+  best_step<kDppQuadXor1>(k, i);
+  best_step<kDppQuadXor2>(k, i);
+  best_step<kDppRowHalfMirror>(k, i);
+  best_step<kDppRowMirror>(k, i);
+  double bk = lane_of(k, 0);
+  int bi = lane_of(i, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double ko = __shfl_xor(k, o);
-    const int io = __shfl_xor(i, o);
-    if (beats(ko, io, k, i)) {
-      k = ko;
-      i = io;
+  for (int r = 16; r < 64; r += 16) {
+    const double kr = lane_of(k, r);
+    const int ir = lane_of(i, r);
+    if (beats(kr, ir, bk, bi)) {
+      bk = kr;
+      bi = ir;
     }
   }
+  k = bk;
+  i = bi;
 }
 
 // Two best fp32 keys seen by a lane or a wave, k1 >= k2, equal keys ordered by

@@ -148,7 +148,7 @@ __device__ RowCls classify_slot(const Inputs& in, int p, int b, int lane) {
   // Rows lo..r must all carry a drafted token in [0, V): the request stops at the first
   // row without one.
   bool bad = lane <= c.j && (dwin < 0 || dwin >= in.V);
-  c.D = __shfl(dwin, 0);
+  c.D = lane_of(dwin, 0);
   for (int base = kWave; base <= c.j && !__ballot(bad); base += kWave) {  // windows beyond 64 rows
     const int D = in.dt[max(r - base - lane, 0)];
     bad = base + lane <= c.j && (D < 0 || D >= in.V);
@@ -415,8 +415,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
   const uint64_t fm = __ballot(found);
   const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
-  pp.lt_D = __shfl(ltD, src);
-  pp.ld_D = __shfl(ldD, src);
+  pp.lt_D = lane_of(ltD, src);
+  pp.ld_D = lane_of(ldD, src);
   pp.flags = fm ? 2 : 0;
   if (lane == 0) w.part1[(int64_t)r * in.w1 + g] = pp;  // read by pass 2, after this kernel
 }
@@ -621,9 +621,9 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
         const int src = __ffsll((unsigned long long)m) - 1;
         stop_j = jh + src / nw;
         k = stop_j;
-        q.final_verdict = __shfl(ev.verdict, src);
-        q.stop = RowStat{__shfl(rs.m_t, src), __shfl(rs.mc_t, src), __shfl(rs.m_d, src), __shfl(rs.mc_d, src),
-                         __shfl(rs.s_t, src), __shfl(rs.s_d, src), __shfl(rs.am_t, src), __shfl(rs.am_d, src)};
+        q.final_verdict = lane_of(ev.verdict, src);
+        q.stop = RowStat{lane_of(rs.m_t, src), lane_of(rs.mc_t, src), lane_of(rs.m_d, src), lane_of(rs.mc_d, src),
+                         lane_of(rs.s_t, src), lane_of(rs.s_d, src), lane_of(rs.am_t, src), lane_of(rs.am_d, src)};
         q.stop_half = half;
         q.stop_lane0 = (src / nw) * nw;
         stopped = true;

@@ -79,19 +79,31 @@ __device__ __forceinline__ float uniform_open(uint32_t w) {
   return (float)((w >> 9) * 2u + 1u) * 0x1p-24f;
 }
 
-// fp32 race exponential E = -ln(U) for ranking candidates; the final choice is
-// re-evaluated in fp64. The guard keeps it strictly positive.
-__device__ __forceinline__ float expo32(uint32_t w) {
-  const float e = -__logf(uniform_open(w));
-  return fmaxf(e, 1e-30f);
+// log2 of the race's uniform by the hardware logarithm. Its relative error is about 1e-7
+// over all of U's values, next to 1 included (measured on MI355X against fp64).
+__device__ __forceinline__ float log2_uniform(uint32_t w) { return __builtin_amdgcn_logf(uniform_open(w)); }
+
+constexpr float kLn2f = 0.693147181f;
+constexpr float kLog2Ln2f = -0.528766373f;  // log2(ln 2)
+
+// fp32 race exponential E = -ln(U) = -log2(U) ln 2 for ranking candidates; the final
+// choice is re-evaluated in fp64. The guard keeps it strictly positive.
+__device__ __forceinline__ float expo32(uint32_t w) { return fmaxf(-log2_uniform(w) * kLn2f, 1e-30f); }
+
+// log2(E) = log2(-log2 U) + log2(ln 2), for keys in the log domain.
+__device__ __forceinline__ float log2_expo32(uint32_t w) {
+  return __builtin_amdgcn_logf(fmaxf(-log2_uniform(w), 1e-30f)) + kLog2Ln2f;
 }
 
-// An upper bound on E = -ln(U), for lower bounds on race keys that prune tokens. A
-// relative 1e-3 and an absolute 1e-6 cover the fast logarithm's error, also for U next to
-// 1 where E is about 6e-8 and the logarithm's relative accuracy is poor.
+// An upper bound on E = -ln(U), for lower bounds on race keys that prune tokens. The
+// relative 1e-3 and absolute 1e-6 are far above the fp32 error of expo32.
 __device__ __forceinline__ float expo32_upper(uint32_t w) {
-  return fmaf(-__logf(uniform_open(w)), 1.001f, 1e-6f);
+  return fmaf(-log2_uniform(w) * kLn2f, 1.001f, 1e-6f);
 }
+
+// x / y by the hardware reciprocal (about 1 ulp), for fp32 ranking keys and their bounds,
+// which carry margins far above it.
+__device__ __forceinline__ float div_fast(float x, float y) { return x * __builtin_amdgcn_rcpf(y); }
 
 __device__ __forceinline__ double expo64(uint32_t w) { return -log((double)uniform_open(w)); }
 
@@ -358,6 +370,7 @@ __device__ __forceinline__ Top2 top2_empty() {
 }
 
 __device__ __forceinline__ void top2_push(Top2& t, float k, int i, float a, float b) {
+  if (!(k > t.k2 || (k == t.k2 && i < t.i2))) return;  // most draws: not among the two best
   if (k > t.k1 || (k == t.k1 && i < t.i1)) {
     t.k2 = t.k1;
     t.i2 = t.i1;

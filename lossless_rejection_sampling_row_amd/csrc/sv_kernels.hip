@@ -776,7 +776,7 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
     const float a = l * q.c;
     if (a > -INFINITY) {
       const uint32_t wd = race_word(in.seed, x, q.k, b);
-      top2_push(t, a - __log2f(expo32(wd)), (int)x, l, 0.0f);
+      top2_push(t, a - log2_expo32(wd), (int)x, l, 0.0f);
     }
   }
   double bk;
@@ -787,8 +787,11 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
   return bi;
 }
 
-// Wave gw of the grid serves span gw % w2 of request gw / w2.
-template <typename E, int VEC, int U>
+// Wave gw of the grid serves span gw % w2 of request gw / w2. DIAG is the diagnostic call's
+// kernel: its residual waves also sum the residual mass, which needs every token's p and mu.
+// The plain call's waves skip, by one test in the logit domain, every 16-byte vector that
+// can hold neither a race candidate nor a token that passes the gate.
+template <typename E, int VEC, int U, bool DIAG>
 __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Outputs out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -898,17 +901,32 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       const float mu = qq >= tau ? qq : 0.0f;
       const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
       if (hx[s] >= 0 && rl > 0.0f)
-        kh = fmaxf(kh, rl / expo32_upper(race_word(in.seed, hx[s], q.k, b)) * (1.0f - kKeyErr));
+        kh = fmaxf(kh, div_fast(rl, expo32_upper(race_word(in.seed, hx[s], q.k, b))) * (1.0f - kKeyErr));
     }
     kh = wave_max(kh);
     float pthr = kh * (float)(kEminLow * 0.5);
     float safe = 0.0f;  // lane's best lower bound on a drawn key
+    // Where the gate fails, r = p = 2^(l*c - mct) / s_t, so r >= pthr needs l*c - mct >= sthr.
+    // The margin covers the fp32 error of p.
+    auto sthr_of = [&](float th) __attribute__((always_inline)) {
+      return th > 0.0f ? __log2f((float)((double)th * q.stop.s_t)) - 1e-3f : -INFINITY;
+    };
+    float sthr = sthr_of(pthr);
 
     float rsum = 0.0f;
     Top2 t = top2_empty();
     auto fold_res = [&](const CH (&xt)[U], const CH (&xd)[U], int v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        if (!DIAG) {
+          float mt = xt[u].get(0), md = xd[u].get(0);
+#pragma unroll
+          for (int e = 1; e < VEC; ++e) {
+            mt = fmaxf(mt, xt[u].get(e));
+            md = fmaxf(md, xd[u].get(e));
+          }
+          if (!(fmaf(mt, c, -mct) >= sthr) && !(md >= gate_l)) continue;
+        }
         const int x0 = (v0 + u * kWave) * VEC;
         float rv[VEC], mv[VEC];
         bool gated = false;
@@ -933,7 +951,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
             const float p = rv[gg + e], mu = mv[gg + e];
             rv[gg + e] = fmaxf(p - mu, 0.0f);
             mv[gg + e] = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
-            rsum += rv[gg + e];
+            if (DIAG) rsum += rv[gg + e];
             any |= (rv[gg + e] > 0.0f && rv[gg + e] >= pthr);
           }
           if (any) {
@@ -945,8 +963,8 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
               if (r > 0.0f && r >= pthr) {
                 const int x = xg + e;
                 const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
-                top2_push(t, r / expo32(wd), x, xt[u].get(gg + e), xd[u].get(gg + e));
-                safe = fmaxf(safe, mv[gg + e] / expo32_upper(wd) * (1.0f - kKeyErr));
+                top2_push(t, div_fast(r, expo32(wd)), x, xt[u].get(gg + e), xd[u].get(gg + e));
+                safe = fmaxf(safe, div_fast(mv[gg + e], expo32_upper(wd)) * (1.0f - kKeyErr));
               }
             }
           }
@@ -966,8 +984,9 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       mask_chunks(db, base + step, lane, sp.end);
       fold_res(tb, db, base + step + lane);
       pthr = fmaxf(pthr, wave_max(safe) * (float)(kEminLow * 0.5));
+      if (!DIAG) sthr = sthr_of(pthr);
     }
-    part.rsum = wave_sum(rsum);
+    part.rsum = DIAG ? wave_sum(rsum) : 0.0f;
     double bk;
     int bi;
     resolve_race(t, wave_max(t.k1) * (1.0f - kRatioKeySlack),
@@ -1017,7 +1036,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
                 if (av[e] + 25.0f >= lb) {
                   const int x = xg + e;
                   const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
-                  const float key = av[e] - __log2f(expo32(wd));
+                  const float key = av[e] - log2_expo32(wd);
                   lbest = fmaxf(lbest, key);
                   top2_push(t, key, x, xt[u].get(gg + e), 0.0f);
                 }
@@ -1070,16 +1089,18 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     int bi = INT32_MAX;
     for (int i = lane; i < nw; i += kWave) {
       const P2Part c2 = read_record(pp + i);
-      R += (double)c2.rsum;
+      if (DIAG) R += (double)c2.rsum;
       if (c2.idx >= 0 && beats(c2.key, c2.idx, bk, bi)) {
         bk = c2.key;
         bi = c2.idx;
       }
     }
-    R = wave_sum(R);
+    if (DIAG) R = wave_sum(R);
     wave_best(bk, bi);
-    resid = (float)R;
-    if (R > 0.0 && bk > 0.0) token = bi;
+    resid = DIAG ? (float)R : NAN;
+    // A drawn candidate has r > 0 (also in fp32), so a positive best key means the residual
+    // has mass, and no candidate means none outside decision-boundary requests.
+    if (bk > 0.0) token = bi;
     else token = p_race_one_wave(in, q, b, lane);  // residual with no mass: race over p
   } else {
     float M = -INFINITY;
@@ -1195,7 +1216,9 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   constexpr int U1 = VEC == 1 ? 8 : 2;  // pass 1: chunks per lane per array and step (x2 buffers)
   constexpr int U2 = VEC == 1 ? 8 : 2;  // pass 2: the same
   const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
-  const void* k2 = reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2>);
+  const bool diag = out.diag != nullptr;
+  const void* k2 = diag ? reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, true>)
+                        : reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, false>);
   int64_t slots1 = 0, slots2 = 0;
   hipError_t err = resident_waves(k1, kTargetWavesPerCU, &slots1);
   if (err != hipSuccess) return err;
@@ -1208,7 +1231,10 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   hipLaunchKernelGGL((pass1_kernel<E, VEC, U1>), dim3((unsigned)l.blocks1), block, 0, stream, in, w, out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
-  hipLaunchKernelGGL((pass2_kernel<E, VEC, U2>), dim3((unsigned)l.blocks2), block, 0, stream, in, w, out);
+  if (diag)
+    hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, true>), dim3((unsigned)l.blocks2), block, 0, stream, in, w, out);
+  else
+    hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, false>), dim3((unsigned)l.blocks2), block, 0, stream, in, w, out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
   return hipSuccess;

@@ -87,18 +87,23 @@ def acceptance_probability(p, q, tau):
     return sum(min(a, b) for a, b in zip(p, mu))
 
 
-def window_law(ps, qs, tau, rule="mu"):
+def window_law(ps, qs, tau, rule="mu", tau_steps=None, min_cum=Fraction(0)):
     """Exact law of (accept_len, emitted tokens) for a window of n rows.
 
     ``ps`` has n target laws (row n-1 is the bonus row). ``qs`` has n-1 draft
     laws, one per proposal row. Rows are verified in order, and the first
     row that does not accept ends the window. Returns {(k, tokens): prob}.
+
+    ``tau_steps`` (n-1 thresholds) replaces ``tau`` row by row, and a positive
+    ``min_cum`` adds the cumulative gate: row j gates at
+    max(step threshold, min_cum / prod_{i<j} q_i(D_i)) over the accepted prefix
+    (regolith audit, section schedule behavior).
     """
     n = len(ps)
     assert len(qs) == n - 1
     out = {}
 
-    def walk(j, prefix, prob):
+    def walk(j, prefix, prob, cum=Fraction(1)):
         if prob == 0:
             return
         if j == n - 1:
@@ -107,13 +112,16 @@ def window_law(ps, qs, tau, rule="mu"):
                     key = (j, tuple(prefix) + (x,))
                     out[key] = out.get(key, Fraction(0)) + prob * px
             return
-        accepted, fallback = row_law(ps[j], qs[j], tau, rule)
+        tau_j = tau if tau_steps is None else tau_steps[j]
+        if min_cum > 0:
+            tau_j = max(tau_j, min_cum / cum)
+        accepted, fallback = row_law(ps[j], qs[j], tau_j, rule)
         for x, fx in enumerate(fallback):
             if fx:
                 key = (j, tuple(prefix) + (x,))
                 out[key] = out.get(key, Fraction(0)) + prob * fx
         for D, aD in enumerate(accepted):
-            walk(j + 1, prefix + [D], prob * aD)
+            walk(j + 1, prefix + [D], prob * aD, cum * qs[j][D])
 
     walk(0, [], Fraction(1))
     return out

@@ -16,7 +16,16 @@ float64 without rounding. Citations name the page and the section:
   proposal stays an ordinary target (bonus) sample.
 * regolith audit "rank-1 moce and step-aware speculative retention",
   section schedule behavior. Equality passes the gate, and a failed gate ends
-  the contiguous prefix.
+  the contiguous prefix. The same section describes two optional knobs,
+  taken here as inputs: a per-step threshold that overrides the request's
+  tau for its row, and a cumulative floor on the product of the draft
+  probabilities of the drafted tokens so far, this row's included, computed
+  in double and reset for every window. Both gates must pass. For row j the
+  product condition q_0(D_0) ... q_j(D_j) >= min_cum is a threshold on
+  q_j(D_j). Gating mu_j with that same threshold,
+      tau_j = max(step threshold, min_cum / (q_0(D_0) ... q_{j-1}(D_{j-1}))),
+  keeps the method lossless: tau_j depends only on the accepted prefix.
+  A floor of 0 disables the cumulative gate.
 * mlxcel PR #992, section What changed. The accept test compares a uniform
   against p and q in the form u*q(t) <= p(t) and requires p(t) > 0, so that a
   q that underflowed to zero cannot admit a token with p = 0. This oracle uses
@@ -38,7 +47,9 @@ Readings where the pages leave a step open:
 * A residual with zero total mass falls back to a race over p.
 * draft_tokens[r] == -1, or any id outside [0, V), means "no proposal". Such a
   row, and the last row of every request, is a bonus row: one race over p.
-* Temperature must be 0 or lie in [2**-14, 2**14]. tau must not be NaN.
+* Temperature must be 0 or lie in [2**-14, 2**14]. tau must not be NaN, nor
+  the step threshold of a row the method tests. The cumulative floor must be
+  finite and >= 0.
   Logits must be finite or -inf. A row that contains NaN or +inf, or holds
   only -inf, is invalid, and so is its request. This is checked only on rows
   the method actually evaluates. An invalid request emits nothing: its
@@ -166,12 +177,18 @@ def _top2_gap(keys: np.ndarray, cond: np.ndarray | None):
 
 
 def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau: float,
-                   seed: int, b: int, rule: str = "mu") -> RequestResult:
+                   seed: int, b: int, rule: str = "mu", tau_steps: np.ndarray | None = None,
+                   min_cum: float = 0.0) -> RequestResult:
     """Verify one request's window of rows.
 
     ``tl``, ``dl`` are float64 [n, V] target and draft logits, and ``dt`` is
     [n] draft tokens. Row n-1 is the bonus row. ``b`` is the request's index
     in the batch, which keys its random stream.
+
+    ``tau_steps`` ([n], optional) holds each row's step threshold, which
+    replaces ``tau`` for that row. ``min_cum`` is the cumulative floor (0 turns
+    that gate off). Row j gates at tau_j = max(step threshold, min_cum / the
+    product of q_i(D_i) over the accepted rows i < j).
 
     ``rule`` selects the method ("mu") or a deliberately wrong rule that the
     pages use as a negative control:
@@ -192,18 +209,19 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
     the other way:
 
     * F1: an offered row with |u - p(D)/mu(D)| < eps.
-    * F2: tau > 0 and |q(D) - tau| < eps.
+    * F2: tau_j > 0 and |q(D) - tau_j| < eps.
     * F3: a race whose two best keys k1 >= k2 have (k1 - k2)/k1 < eps * c.
       Here c = max(1, (p+mu)/r) over the two tokens of a residual race with
       r = p - mu. That is the factor by which a relative error of eps in p
       and mu moves the key r/E.
-    * F4: a residual race with some |q_x - tau| < eps (tau > 0), or a
+    * F4: a residual race with some |q_x - tau_j| < eps (tau_j > 0), or a
       residual mass below eps.
     """
     n, V = tl.shape
     res = RequestResult(tokens=[], accept_len=-1)
-    if not temperature_valid(T) or np.isnan(tau):
+    if not temperature_valid(T) or np.isnan(tau) or not (np.isfinite(min_cum) and min_cum >= 0.0):
         return res
+    cum = 1.0  # product of q_i(D_i) over the accepted rows so far
     for j in range(n):
         D = int(dt[j])
         bonus = (j == n - 1) or not (0 <= D < V)
@@ -229,6 +247,13 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
             return res
         q = distribution(dl[j], T)
         rec = RowRecord(j=j, verdict=0, p_D=float(p[D]), q_D=float(q[D]))
+        tau_j = tau if tau_steps is None else float(tau_steps[j])
+        if np.isnan(tau_j):
+            res.tokens = []
+            res.rows.append(RowRecord(j=j, verdict=0))
+            return res
+        if min_cum > 0.0:
+            tau_j = max(tau_j, min_cum / cum)
 
         if rule == "argmax":
             am = argmax_lowest(p)
@@ -243,9 +268,9 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
             res.accept_len = len(res.tokens) - 1
             return res
 
-        mu = retained_measure(q, tau)
-        offered = q[D] >= tau
-        if rule == "mu" and T > 0.0 and tau > 0.0 and abs(q[D] - tau) < FLAG_EPS:
+        mu = retained_measure(q, tau_j)
+        offered = q[D] >= tau_j
+        if rule == "mu" and T > 0.0 and tau_j > 0.0 and abs(q[D] - tau_j) < FLAG_EPS:
             res.flags |= F_GATE
         if offered:
             mu_D = q[D] if rule == "original" else mu[D]
@@ -260,6 +285,7 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
                 rec.verdict = ACCEPT
                 res.rows.append(rec)
                 res.tokens.append(D)
+                cum *= q[D]
                 continue
             rec.verdict = REJECT
         else:
@@ -289,7 +315,7 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
                 gap, c = _top2_gap(p / E, None)
             if gap < FLAG_EPS * c:
                 res.flags |= F_RACE
-            if R < FLAG_EPS or (tau > 0.0 and bool((np.abs(q - tau) < FLAG_EPS).any())):
+            if R < FLAG_EPS or (tau_j > 0.0 and bool((np.abs(q - tau_j) < FLAG_EPS).any())):
                 res.flags |= F_SUPPORT
         res.rows.append(rec)
         res.tokens.append(tok)
@@ -321,12 +347,14 @@ class BatchResult:
 
 
 def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int,
-                 dtype: str, requests=None, rule: str = "mu") -> BatchResult:
+                 dtype: str, requests=None, rule: str = "mu", tau_step=None, min_cum=None) -> BatchResult:
     """Verify every request of a batch (or only those listed in ``requests``).
 
     ``target`` and ``draft`` are [R, V] arrays of bf16 bit patterns (uint16) or
     fp32 values. The other arguments mirror the C-ABI entry point. Requests not
-    in ``requests`` keep -1 outputs.
+    in ``requests`` keep -1 outputs. ``tau_step`` ([R] float32) and ``min_cum``
+    ([B] float32) are the optional per-row step thresholds and per-request
+    cumulative floors.
     """
     target = np.asarray(target)
     R, V = target.shape
@@ -343,12 +371,15 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     temperature = np.asarray(temperature, dtype=np.float32).astype(np.float64)
     tau = np.asarray(tau, dtype=np.float32).astype(np.float64)
     dt = np.asarray(draft_tokens, dtype=np.int64)
+    ts = None if tau_step is None else np.asarray(tau_step, dtype=np.float32).astype(np.float64)
+    mc = None if min_cum is None else np.asarray(min_cum, dtype=np.float32).astype(np.float64)
     todo = range(B) if requests is None else requests
     for b in todo:
         lo, hi = int(ro[b]), int(ro[b + 1])
         tl = decode_logits(target[lo:hi], dtype)
         dl = decode_logits(np.asarray(draft)[lo:hi], dtype)
-        rr = verify_request(tl, dl, dt[lo:hi], float(temperature[b]), float(tau[b]), seed, b, rule)
+        rr = verify_request(tl, dl, dt[lo:hi], float(temperature[b]), float(tau[b]), seed, b, rule,
+                            None if ts is None else ts[lo:hi], 0.0 if mc is None else float(mc[b]))
         flags[b] = rr.flags
         for rec in rr.rows:
             r = lo + rec.j

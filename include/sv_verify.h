@@ -180,6 +180,44 @@ sv_status sv_verify_batch_diag(const void* target_logits, const void* draft_logi
                                sv_row_diag* out_row_diag, sv_batch_stats* out_stats,
                                void* const* hip_events);
 
+/*
+ * sv_verify_batch_sched - sv_verify_batch with a per-step gate schedule and a
+ * cumulative prefix floor, plus optional diagnostics.
+ *
+ * Source: regolith audit "rank-1 moce and step-aware speculative retention",
+ * section schedule behavior. A supplied schedule overrides the request's
+ * threshold per step. The cumulative gate requires the product of the draft
+ * probabilities of the drafted tokens so far, the current one included, to
+ * reach a floor. Both gates must pass, equality passes, and a failed gate ends
+ * the prefix like any NULL row.
+ *
+ * Row j of request b (r = row_offsets[b] + j) offers its drafted token D iff
+ * q(D) >= tau_j, with
+ *     tau_j = max(s_r, m_b / (q_0(D_0) * ... * q_{j-1}(D_{j-1})))   if m_b > 0,
+ *     tau_j = s_r                                                    otherwise,
+ * where s_r = tau_step[r] (tau[b] when tau_step is NULL) and m_b = min_cum[b]
+ * (0 when min_cum is NULL). The product runs over the accepted rows before j,
+ * in fp64. mu = q * [q >= tau_j] on that row, also for its residual draw, so
+ * the method stays lossless: tau_j depends only on the accepted prefix.
+ *
+ * tau_step   [R] float (device), or NULL. A schedule of thresholds for steps
+ *            0, 1, 2, ... with its last entry repeating is expanded into it by
+ *            the caller. Entries of bonus rows are ignored. A NaN entry on a
+ *            row the method tests fails its request closed.
+ * min_cum    [B] float (device), or NULL. 0 turns the cumulative gate off; a
+ *            value that is NaN, infinite or negative fails its request closed.
+ * Every other argument, the results, ownership, the workspace and the errors
+ * are those of sv_verify_batch_diag (without events). With both tau_step and
+ * min_cum NULL it computes exactly what sv_verify_batch_diag computes.
+ */
+sv_status sv_verify_batch_sched(const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* row_offsets,
+                                const float* temperature, const float* tau, const float* tau_step,
+                                const float* min_cum, uint64_t seed, int32_t* out_tokens,
+                                int32_t* out_accept_len, sv_shape shape, void* workspace,
+                                size_t workspace_bytes, void* hip_stream, sv_row_diag* out_row_diag,
+                                sv_batch_stats* out_stats);
+
 /* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
 size_t sv_workspace_bytes(sv_shape shape);
 

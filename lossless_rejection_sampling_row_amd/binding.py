@@ -50,6 +50,10 @@ def load_library():
     lib.sv_verify_batch.restype = c_int
     lib.sv_verify_batch_diag.argtypes = common + [c_void_p, c_void_p, POINTER(c_void_p)]
     lib.sv_verify_batch_diag.restype = c_int
+    sched = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_uint64,
+             c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]
+    lib.sv_verify_batch_sched.argtypes = sched
+    lib.sv_verify_batch_sched.restype = c_int
     lib.sv_workspace_bytes.argtypes = [SvShape]
     lib.sv_workspace_bytes.restype = c_size_t
     lib.sv_status_string.argtypes = [c_int]
@@ -105,7 +109,7 @@ def _ptr(t):
 
 def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int, *,
                  out_tokens=None, out_accept_len=None, workspace=None, row_diag=None, stats=None,
-                 events=None, stream=None):
+                 events=None, stream=None, tau_step=None, min_cum=None):
     """Verify a batch of speculative windows on the GPU.
 
     target, draft : [R, V] bfloat16 or float32 (same dtype), row-major, on one GPU.
@@ -117,6 +121,9 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     row_diag      : optional [R, 8] int32 tensor that receives sv_row_diag records.
     stats         : optional [8] int64 tensor that receives sv_batch_stats.
     events        : optional sequence of three raw hipEvent_t handles (ints).
+    tau_step      : optional [R] float32 per-row gate thresholds (see expand_schedule).
+    min_cum       : optional [B] float32 cumulative floors (0 = off).
+    With tau_step or min_cum the call goes to sv_verify_batch_sched (no events).
     stream        : optional torch stream (default: the current stream).
 
     Returns (out_tokens [R] int32, out_accept_len [B] int32). Work is enqueued
@@ -133,10 +140,13 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
         raise ValueError("logits must be [R, V]")
     R, V = int(target.shape[0]), int(target.shape[1])
     B = int(row_offsets.numel()) - 1
-    for name, t, dt, n in (("draft_tokens", draft_tokens, torch.int32, R),
-                           ("row_offsets", row_offsets, torch.int32, B + 1),
-                           ("temperature", temperature, torch.float32, B),
-                           ("tau", tau, torch.float32, B)):
+    checks = [("draft_tokens", draft_tokens, torch.int32, R), ("row_offsets", row_offsets, torch.int32, B + 1),
+              ("temperature", temperature, torch.float32, B), ("tau", tau, torch.float32, B)]
+    if tau_step is not None:
+        checks.append(("tau_step", tau_step, torch.float32, R))
+    if min_cum is not None:
+        checks.append(("min_cum", min_cum, torch.float32, B))
+    for name, t, dt, n in checks:
         if t.dtype != dt or t.numel() != n or t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name}: expected contiguous {dt} [{n}] on {dev}")
     if not (target.is_contiguous() and draft.is_contiguous()):
@@ -156,19 +166,43 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
             _ptr(tau), c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(out_tokens),
             _ptr(out_accept_len), shape, _ptr(workspace), c_size_t(workspace.numel()),
             c_void_p(stream.cuda_stream)]
-    if row_diag is None and stats is None and events is None:
+    if row_diag is not None and (row_diag.dtype != torch.int32 or row_diag.numel() != 8 * R):
+        raise ValueError("row_diag must be an int32 tensor with 8*R elements")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() != 8):
+        raise ValueError("stats must be an int64 tensor with 8 elements")
+    if tau_step is not None or min_cum is not None:
+        if events is not None:
+            raise ValueError("events are not supported together with tau_step / min_cum")
+        sargs = args[:6] + [_ptr(tau_step) if tau_step is not None else None,
+                            _ptr(min_cum) if min_cum is not None else None] + args[6:]
+        _check(lib.sv_verify_batch_sched(*sargs, _ptr(row_diag) if row_diag is not None else None,
+                                         _ptr(stats) if stats is not None else None))
+    elif row_diag is None and stats is None and events is None:
         _check(lib.sv_verify_batch(*args))
     else:
-        if row_diag is not None and (row_diag.dtype != torch.int32 or row_diag.numel() != 8 * R):
-            raise ValueError("row_diag must be an int32 tensor with 8*R elements")
-        if stats is not None and (stats.dtype != torch.int64 or stats.numel() != 8):
-            raise ValueError("stats must be an int64 tensor with 8 elements")
         ev = None
         if events is not None:
             ev = (c_void_p * 3)(*[c_void_p(int(e)) for e in events])
         _check(lib.sv_verify_batch_diag(*args, _ptr(row_diag) if row_diag is not None else None,
                                         _ptr(stats) if stats is not None else None, ev))
     return out_tokens, out_accept_len
+
+
+def expand_schedule(schedule, row_offsets):
+    """Per-row gate thresholds from a step schedule: row j of every request gets
+    schedule[min(j, len(schedule) - 1)], the last threshold repeating for later steps
+    (regolith audit "rank-1 moce and step-aware speculative retention", section schedule
+    behavior). ``row_offsets`` is a host sequence; returns a host float32 numpy array [R]."""
+    import numpy as np
+    sched = [float(x) for x in schedule]
+    if not 1 <= len(sched) <= 8:
+        raise ValueError("a schedule has one to eight thresholds")
+    ro = [int(x) for x in row_offsets]
+    out = np.empty(ro[-1], dtype=np.float32)
+    for b in range(len(ro) - 1):
+        for j in range(ro[b + 1] - ro[b]):
+            out[ro[b] + j] = sched[min(j, len(sched) - 1)]
+    return out
 
 
 def split_row_diag(row_diag):

@@ -43,6 +43,8 @@ struct Inputs {
   const int32_t* ro;
   const float* temp;
   const float* tau;
+  const float* tau_step;  // [R] per-row step thresholds, or null (tau[b] for every row)
+  const float* min_cum;   // [B] cumulative floors, or null (no cumulative gate)
   uint64_t seed;
   int32_t B, R, V, dtype;
   int32_t w1;  // pass 1: waves per row
@@ -433,6 +435,7 @@ struct RowStat {
 struct RowEval {
   int verdict;
   float p_D, q_D, mu_D, u;
+  float tau_eff;  // the row's gate threshold
 };
 
 // Merge the partials of the rows held by this wave and test each row's drafted token, all
@@ -441,8 +444,17 @@ struct RowEval {
 // whose row is to be tested. Each group reduces in a fixed order with fp64 sums, so every
 // lane of a group ends with its row's result. j is the lane's row position in the request
 // and D its drafted token.
+//
+// The gate threshold of row j is its step threshold ts, raised by the cumulative floor to
+// floor / (q_0(D_0) ... q_{j-1}(D_{j-1})) when floor > 0 (regolith audit, section schedule
+// behavior: the product of the drafted tokens' probabilities, this row's included, must
+// reach the floor). `carry` is that product over the rows before this slot set, and
+// `nlive` the number of live rows in the set; `carry` returns multiplied by the set's rows.
+// Without SCHED the threshold is ts on every row (no floor), as in the plain call.
+template <bool SCHED>
 __device__ __forceinline__ RowEval eval_rows(const Inputs& in, const P1Part& e, bool live, int nw, int b, int j,
-                                             int D, float T, float tau, float c, RowStat& rs) {
+                                             int D, float T, float ts, float floor, double& carry, int nlive,
+                                             float c, RowStat& rs) {
   const bool greedy = T == 0.0f;
   const float mt = seg_max(live ? e.m_t : -INFINITY, nw);
   const float md = seg_max(live ? e.m_d : -INFINITY, nw);
@@ -468,21 +480,41 @@ __device__ __forceinline__ RowEval eval_rows(const Inputs& in, const P1Part& e, 
   rs = RowStat{mt, mct, md, mcd, st, sd, it == INT32_MAX ? -1 : it, id == INT32_MAX ? -1 : id};
 
   const bool valid = __builtin_isfinite(mt) && __builtin_isfinite(md) && __builtin_isfinite(st) && st > 0.0 &&
-                     __builtin_isfinite(sd) && sd > 0.0 && nf == 1;
+                     __builtin_isfinite(sd) && sd > 0.0 && nf == 1 && !__builtin_isnan(ts);
   RowEval ev{};
   ev.u = NAN;
+  double p, q;
+  if (greedy) {  // one-hot p and q
+    p = (D == rs.am_t) ? 1.0 : 0.0;
+    q = (D == rs.am_d) ? 1.0 : 0.0;
+  } else {
+    p = exp2((double)ltD * (double)c - (double)mct) / st;
+    q = exp2((double)ldD * (double)c - (double)mcd) / sd;
+  }
+  // Row group g of the set sits in lanes g*nw .. g*nw + nw - 1; every lane of a group holds
+  // its row's q. The product runs over the live rows before this lane's row, in row order.
+  double tau_eff = (double)ts;
+  if (SCHED && floor > 0.0f) {
+    double pre = carry;
+    const int jj = (int)(threadIdx.x & (kWave - 1)) / nw;
+    for (int g = 0; g < nlive; ++g) {
+      const double qg = lane_of(q, g * nw);
+      if (g < jj) pre *= qg;
+      carry *= qg;
+    }
+    tau_eff = fmax(tau_eff, (double)floor / pre);
+  }
+  ev.tau_eff = (float)tau_eff;
   if (greedy) {
-    ev.p_D = (D == rs.am_t) ? 1.0f : 0.0f;
-    ev.q_D = (D == rs.am_d) ? 1.0f : 0.0f;
-    const bool offered = ev.q_D >= tau;
+    ev.p_D = (float)p;
+    ev.q_D = (float)q;
+    const bool offered = q >= tau_eff;
     ev.mu_D = offered ? ev.q_D : 0.0f;
     // p(D) is 0 or 1 and mu(D) <= 1: u*mu(D) < p(D) holds for every u iff p(D) = 1.
     ev.verdict = !valid ? kRowInvalid : !offered ? SV_ROW_NULL : (ev.p_D == 1.0f ? SV_ROW_ACCEPT : SV_ROW_REJECT);
     return ev;
   }
-  const double p = exp2((double)ltD * (double)c - (double)mct) / st;
-  const double q = exp2((double)ldD * (double)c - (double)mcd) / sd;
-  const bool offered = q >= (double)tau;
+  const bool offered = q >= tau_eff;
   const double mu = offered ? q : 0.0;
   ev.p_D = (float)p;
   ev.q_D = (float)q;
@@ -520,6 +552,7 @@ __device__ __forceinline__ P1Part pick_part(bool second, const P1Part& a, const 
 struct ReqHead {
   int lo, n;
   float T, tau;
+  float floor;  // cumulative floor (0: no cumulative gate)
 };
 
 __device__ __forceinline__ ReqHead request_head(const Inputs& in, int b) {
@@ -528,6 +561,7 @@ __device__ __forceinline__ ReqHead request_head(const Inputs& in, int b) {
   h.n = in.ro[b + 1] - h.lo;
   h.T = in.temp[b];
   h.tau = in.tau[b];
+  h.floor = in.min_cum != nullptr ? in.min_cum[b] : 0.0f;
   return h;
 }
 
@@ -538,7 +572,8 @@ struct ReqState {
   int f;              // the row that yields the last token (lo + k)
   int kind;           // kKind*
   int final_verdict;  // verdict of row f (SV_ROW_BONUS when every proposal row was accepted)
-  float T, tau, c;
+  float T, tau, c;    // after the walk, tau is row f's gate threshold
+  float floor;        // cumulative floor
   RowStat stop;       // row f's statistics when f is a proposal row
   int stop_half;      // row f's partials are in e1 (1) or e0 (0) ...
   int stop_lane0;     // ... in lanes stop_lane0 .. stop_lane0 + w1 - 1
@@ -548,9 +583,11 @@ struct ReqState {
 // rows lo .. lo + 128/w1 - 1 in two slots per lane: e0 holds rows lo .. lo + 64/w1 - 1,
 // e1 the next 64/w1 rows, one partial per lane. Indices are clamped into the arrays, so
 // this may run before lo is known to be right.
+template <bool SCHED>
 __device__ __forceinline__ void prefetch_rows(const Inputs& in, const Work& w, int lo, int lane, int& dt0,
-                                              P1Part& e0, P1Part& e1) {
+                                              float& ts0, P1Part& e0, P1Part& e1) {
   dt0 = in.dt[min(lo + lane, in.R - 1)];
+  ts0 = SCHED && in.tau_step != nullptr ? in.tau_step[min(lo + lane, in.R - 1)] : 0.0f;
   const int64_t base = (int64_t)lo * in.w1;
   const int64_t last = (int64_t)in.R * in.w1 - 1;
   e0 = w.part1[min(base + lane, last)];
@@ -564,23 +601,26 @@ __device__ __forceinline__ void prefetch_rows(const Inputs& in, const Work& w, i
 // one slot are tested together. On return e0/e1 hold the slot set with row f. With
 // `diag`, each row's record is written once: tested rows by their group's first lane (the
 // stop row with `stop_resid`), untested and bonus rows after the walk.
+template <bool SCHED>
 __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w, int b, const ReqHead& h,
-                                                 int lo_pre, int lane, int dt0, P1Part& e0, P1Part& e1,
+                                                 int lo_pre, int lane, int dt0, float ts0, P1Part& e0, P1Part& e1,
                                                  sv_row_diag* diag, float stop_resid) {
   ReqState q{};
   q.lo = h.lo;
   q.n = h.n;
   q.T = h.T;
   q.tau = h.tau;
+  q.floor = SCHED ? h.floor : 0.0f;
   q.stop_half = 0;
   q.stop_lane0 = 0;
-  const bool req_ok = temperature_ok(q.T) && !__builtin_isnan(q.tau);
+  const bool req_ok = temperature_ok(q.T) && !__builtin_isnan(q.tau) && __builtin_isfinite(q.floor) &&
+                      q.floor >= 0.0f;
   q.c = req_ok ? fold_scale(q.T) : 0.0f;
   const int nw = in.w1;
   const int rows_half = kWave / nw;
   const int per_group = 2 * rows_half;
   const int nd = q.n - 1;  // rows that carry a drafted token: all but the last
-  if (q.lo != lo_pre) prefetch_rows(in, w, q.lo, lane, dt0, e0, e1);  // requests of different lengths
+  if (q.lo != lo_pre) prefetch_rows<SCHED>(in, w, q.lo, lane, dt0, ts0, e0, e1);  // requests of different lengths
   // Proposal rows: the rows before the first drafted token outside [0, V).
   q.n_prop = nd;
   for (int base = 0; base < nd; base += kWave) {
@@ -599,11 +639,14 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   }
   int k = q.n_prop;
   bool stopped = false;
+  float stop_tau = q.tau;
+  double carry = 1.0;  // product of q(D) over the rows before the current slot set
   const int jj = lane / nw;  // the lane's row within a slot set
   for (int j0 = 0; j0 < q.n_prop && !stopped; j0 += per_group) {
     if (j0 > 0) {  // windows longer than one group
       int unused;
-      prefetch_rows(in, w, q.lo + j0, lane, unused, e0, e1);
+      float unused_ts;
+      prefetch_rows<SCHED>(in, w, q.lo + j0, lane, unused, unused_ts, e0, e1);
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {  // unrolled: e0 and e1 stay in registers
@@ -613,8 +656,12 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
       const bool live = j < q.n_prop;
       const int jc = min(j, nd - 1);
       const int D = jc < kWave ? __shfl(dt0, jc) : in.dt[q.lo + jc];
+      const float ts = !SCHED || in.tau_step == nullptr ? q.tau
+                                                        : jc < kWave ? __shfl(ts0, jc) : in.tau_step[q.lo + jc];
+      const int nlive = min(rows_half, q.n_prop - jh);
       RowStat rs;
-      const RowEval ev = eval_rows(in, pick_part(half != 0, e0, e1), live, nw, b, j, D, q.T, q.tau, q.c, rs);
+      const RowEval ev = eval_rows<SCHED>(in, pick_part(half != 0, e0, e1), live, nw, b, j, D, q.T, ts, q.floor, carry,
+                                   nlive, q.c, rs);
       const uint64_t m = __ballot(live && ev.verdict != SV_ROW_ACCEPT);
       int stop_j = INT32_MAX;
       if (m != 0) {
@@ -622,6 +669,7 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
         stop_j = jh + src / nw;
         k = stop_j;
         q.final_verdict = lane_of(ev.verdict, src);
+        stop_tau = lane_of(ev.tau_eff, src);
         q.stop = RowStat{lane_of(rs.m_t, src), lane_of(rs.mc_t, src), lane_of(rs.m_d, src), lane_of(rs.mc_d, src),
                          lane_of(rs.s_t, src), lane_of(rs.s_d, src), lane_of(rs.am_t, src), lane_of(rs.am_d, src)};
         q.stop_half = half;
@@ -644,6 +692,7 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   }
   q.k = k;
   q.f = q.lo + k;
+  q.tau = stop_tau;
   const bool greedy = q.T == 0.0f;
   if (k < q.n_prop) {
     q.kind = q.final_verdict == kRowInvalid ? kKindInvalid : greedy ? kKindGreedyDone : kKindResidual;
@@ -668,6 +717,7 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   q.f = uni(q.f);
   q.kind = uni(q.kind);
   q.final_verdict = uni(q.final_verdict);
+  q.tau = uni(q.tau);
   q.stop.m_t = uni(q.stop.m_t);
   q.stop.mc_t = uni(q.stop.mc_t);
   q.stop.m_d = uni(q.stop.m_d);
@@ -715,9 +765,10 @@ __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, co
       for (int j = lane; j < q.n; j += kWave) out.diag[q.lo + j] = untested_diag();
     } else {
       int dt0;
+      float ts0;
       P1Part e0, e1;
-      prefetch_rows(in, w, q.lo, lane, dt0, e0, e1);
-      walk_request(in, w, b, request_head(in, b), q.lo, lane, dt0, e0, e1, out.diag, resid);
+      prefetch_rows<true>(in, w, q.lo, lane, dt0, ts0, e0, e1);
+      walk_request<true>(in, w, b, request_head(in, b), q.lo, lane, dt0, ts0, e0, e1, out.diag, resid);
     }
   }
 }
@@ -787,8 +838,10 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
   return bi;
 }
 
-// Wave gw of the grid serves span gw % w2 of request gw / w2. DIAG is the diagnostic call's
-// kernel: its residual waves also sum the residual mass, which needs every token's p and mu.
+// Wave gw of the grid serves span gw % w2 of request gw / w2. DIAG is the kernel of the
+// diagnostic and scheduled calls: its residual waves also sum the residual mass, which needs
+// every token's p and mu, and its walk applies per-row step thresholds and the cumulative
+// floor.
 // The plain call's waves skip, by one test in the logit domain, every 16-byte vector that
 // can hold neither a race candidate nor a token that passes the gate.
 template <typename E, int VEC, int U, bool DIAG>
@@ -808,8 +861,9 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   const ReqHead rh = request_head(in, b);
   const int lo_pre = (int)((int64_t)b * in.R / in.B);
   int dt0;
+  float ts0;
   P1Part e0, e1;
-  prefetch_rows(in, w, lo_pre, lane, dt0, e0, e1);
+  prefetch_rows<DIAG>(in, w, lo_pre, lane, dt0, ts0, e0, e1);
   if (!ro_valid) {
     // Broken row_offsets: the whole batch fails closed. The head wave of request b
     // clears an even share of the rows.
@@ -827,7 +881,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     return;
   }
 
-  const ReqState q = walk_request(in, w, b, rh, lo_pre, lane, dt0, e0, e1, nullptr, NAN);
+  const ReqState q = walk_request<DIAG>(in, w, b, rh, lo_pre, lane, dt0, ts0, e0, e1, nullptr, NAN);
   if (q.kind == kKindInvalid) {
     if (head) emit_request(in, w, out, b, q, true, -1, NAN, lane);
     return;
@@ -1216,7 +1270,7 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   constexpr int U1 = VEC == 1 ? 8 : 2;  // pass 1: chunks per lane per array and step (x2 buffers)
   constexpr int U2 = VEC == 1 ? 8 : 2;  // pass 2: the same
   const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
-  const bool diag = out.diag != nullptr;
+  const bool diag = out.diag != nullptr || in.tau_step != nullptr || in.min_cum != nullptr;
   const void* k2 = diag ? reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, true>)
                         : reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, false>);
   int64_t slots1 = 0, slots2 = 0;
@@ -1242,6 +1296,7 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
 
 static sv_status run(const void* target, const void* draft, const int32_t* draft_tokens,
                      const int32_t* row_offsets, const float* temperature, const float* tau,
+                     const float* tau_step, const float* min_cum,
                      uint64_t seed, int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
                      void* workspace, size_t workspace_bytes, void* hip_stream,
                      sv_row_diag* diag, sv_batch_stats* stats, void* const* events) {
@@ -1251,7 +1306,8 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
   if (st != SV_OK) return st;
   if (shape.B == 0) return SV_OK;
   char* ws = static_cast<char*>(workspace);
-  Inputs in{target, draft, draft_tokens, row_offsets, temperature, tau, seed, p.B, p.R, p.V, p.dtype, 1, 1};
+  Inputs in{target, draft, draft_tokens, row_offsets, temperature, tau, tau_step, min_cum,
+            seed, p.B, p.R, p.V, p.dtype, 1, 1};
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
          reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2)};
   Outputs out{out_tokens, out_accept_len, diag, stats};
@@ -1280,8 +1336,8 @@ extern "C" sv_status sv_verify_batch(const void* target_logits, const void* draf
                                      const float* temperature, const float* tau, uint64_t seed,
                                      int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
-  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, seed,
-                 out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
+  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, nullptr, nullptr,
+                 seed, out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
                  nullptr, nullptr, nullptr);
 }
 
@@ -1292,7 +1348,19 @@ extern "C" sv_status sv_verify_batch_diag(const void* target_logits, const void*
                                           sv_shape shape, void* workspace, size_t workspace_bytes,
                                           void* hip_stream, sv_row_diag* out_row_diag,
                                           sv_batch_stats* out_stats, void* const* hip_events) {
-  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, seed,
-                 out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
+  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, nullptr, nullptr,
+                 seed, out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
                  out_row_diag, out_stats, hip_events);
+}
+
+extern "C" sv_status sv_verify_batch_sched(const void* target_logits, const void* draft_logits,
+                                           const int32_t* draft_tokens, const int32_t* row_offsets,
+                                           const float* temperature, const float* tau, const float* tau_step,
+                                           const float* min_cum, uint64_t seed, int32_t* out_tokens,
+                                           int32_t* out_accept_len, sv_shape shape, void* workspace,
+                                           size_t workspace_bytes, void* hip_stream, sv_row_diag* out_row_diag,
+                                           sv_batch_stats* out_stats) {
+  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, tau_step, min_cum,
+                 seed, out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
+                 out_row_diag, out_stats, nullptr);
 }

@@ -43,6 +43,9 @@ def upload(batch, device="cuda"):
         temperature=torch.from_numpy(np.ascontiguousarray(batch["temperature"], dtype=np.float32)).to(device),
         tau=torch.from_numpy(np.ascontiguousarray(batch["tau"], dtype=np.float32)).to(device),
     )
+    for key in ("tau_step", "min_cum"):  # optional gate schedule and cumulative floor
+        if batch.get(key) is not None:
+            g[key] = torch.from_numpy(np.ascontiguousarray(batch[key], dtype=np.float32)).to(device)
     return g
 
 
@@ -68,7 +71,8 @@ def run_gpu(batch, seed=None, gpu=None, diag=True):
     stats = torch.full((8,), -7, dtype=torch.int64, device="cuda") if diag else None
     toks, lens = binding.verify_batch(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"],
                                       g["temperature"], g["tau"], batch["seed"] if seed is None else seed,
-                                      row_diag=row_diag, stats=stats)
+                                      row_diag=row_diag, stats=stats, tau_step=g.get("tau_step"),
+                                      min_cum=g.get("min_cum"))
     torch.cuda.synchronize()
     if diag:
         p, q, mu, u, rm, v = binding.split_row_diag(row_diag)
@@ -82,7 +86,8 @@ def run_gpu(batch, seed=None, gpu=None, diag=True):
 def run_oracle(batch, seed=None, requests=None):
     return ov.verify_batch(batch["target"], batch["draft"], batch["draft_tokens"], batch["row_offsets"],
                            batch["temperature"], batch["tau"], batch["seed"] if seed is None else seed,
-                           batch["dtype"], requests=requests)
+                           batch["dtype"], requests=requests, tau_step=batch.get("tau_step"),
+                           min_cum=batch.get("min_cum"))
 
 
 @dataclass

@@ -406,3 +406,59 @@ def acceptance_probability(p: np.ndarray, mu: np.ndarray) -> float:
 def sum_prod(p: np.ndarray, q: np.ndarray) -> float:
     """sum_x p(x) q(x): acceptance of the sampler-match rule (mlxcel PR #992, The acceptance ceiling)."""
     return float((p * q).sum())
+
+
+def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: str,
+             tau_step=None, min_cum=None):
+    """Per proposal row: sum_x min(p(x), mu(x)) and sum_x p(x) q(x).
+
+    The first is the probability that the row accepts its draft given that its
+    prefix was accepted (Strata PR #3416, section Approach; mlxcel PR #992,
+    section The acceptance ceiling); the second is the sampler-match rule's.
+    mu uses the row's gate threshold: its step threshold (tau[b] without one),
+    raised by the cumulative floor over the drafted tokens before it, as in
+    ``verify_request``. Proposal rows are the rows before a request's first
+    row without a proposal and before its last row; every other row gets NaN.
+    A request that ``verify_request`` would fail closed on its knobs, or a row
+    whose logits are invalid, gets NaN.
+    """
+    target = np.asarray(target)
+    R, V = target.shape
+    ro = np.asarray(row_offsets, dtype=np.int64)
+    B = ro.size - 1
+    smin = np.full(R, np.nan)
+    spq = np.full(R, np.nan)
+    if not row_offsets_valid(ro, R):
+        return smin, spq
+    temperature = np.asarray(temperature, dtype=np.float32).astype(np.float64)
+    tau = np.asarray(tau, dtype=np.float32).astype(np.float64)
+    dt = np.asarray(draft_tokens, dtype=np.int64)
+    ts = None if tau_step is None else np.asarray(tau_step, dtype=np.float32).astype(np.float64)
+    mc = None if min_cum is None else np.asarray(min_cum, dtype=np.float32).astype(np.float64)
+    for b in range(B):
+        lo, hi = int(ro[b]), int(ro[b + 1])
+        T = float(temperature[b])
+        floor = 0.0 if mc is None else float(mc[b])
+        if not temperature_valid(T) or np.isnan(tau[b]) or not (np.isfinite(floor) and floor >= 0.0):
+            continue
+        cum = 1.0
+        for j in range(hi - lo - 1):
+            r = lo + j
+            D = int(dt[r])
+            if not 0 <= D < V:
+                break
+            tl = decode_logits(target[r:r + 1], dtype)[0]
+            dl = decode_logits(np.asarray(draft)[r:r + 1], dtype)[0]
+            if not (row_valid(tl) and row_valid(dl)):
+                break
+            p = distribution(tl, T)
+            q = distribution(dl, T)
+            tau_j = float(tau[b]) if ts is None else float(ts[r])
+            if np.isnan(tau_j):
+                break
+            if floor > 0.0:
+                tau_j = max(tau_j, floor / cum)
+            smin[r] = acceptance_probability(p, retained_measure(q, tau_j))
+            spq[r] = sum_prod(p, q)
+            cum *= q[D]
+    return smin, spq

@@ -218,6 +218,34 @@ sv_status sv_verify_batch_sched(const void* target_logits, const void* draft_log
                                 size_t workspace_bytes, void* hip_stream, sv_row_diag* out_row_diag,
                                 sv_batch_stats* out_stats);
 
+/*
+ * sv_row_acceptance - per-row acceptance sums of a verify batch.
+ *
+ * For every proposal row r (row j of request b; the rows before a request's
+ * first row without a proposal and before its last row):
+ *   out_sum_min[r] = sum_x min(p(x), mu(x)): the probability that row r
+ *                    accepts its draft given that its prefix was accepted
+ *                    (Strata PR #3416, section Approach; mlxcel PR #992,
+ *                    section The acceptance ceiling);
+ *   out_sum_pq[r]  = sum_x p(x) q(x): the sampler-match rule's acceptance
+ *                    (mlxcel PR #992, same section).
+ * p and q are softmax(logits / T_b) (one-hot argmaxes at T_b = 0), and mu is
+ * q gated at row r's threshold as in sv_verify_batch_sched, with the drafted
+ * tokens as the prefix. Every other row gets NaN. So does a row of a request
+ * whose T_b, tau_b or floor is invalid, and a row with an invalid row up to it
+ * (NaN or +inf or all -inf logits, or a NaN step threshold). Broken
+ * row_offsets make every row NaN.
+ * out_sum_min, out_sum_pq   [R] float (device), written in full.
+ * tau_step, min_cum         as in sv_verify_batch_sched (each may be NULL).
+ * It reads every proposal row twice (statistics, then sums) and draws no
+ * random numbers. Arguments, workspace and errors are as for sv_verify_batch.
+ */
+sv_status sv_row_acceptance(const void* target_logits, const void* draft_logits,
+                            const int32_t* draft_tokens, const int32_t* row_offsets,
+                            const float* temperature, const float* tau, const float* tau_step,
+                            const float* min_cum, float* out_sum_min, float* out_sum_pq,
+                            sv_shape shape, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
 size_t sv_workspace_bytes(sv_shape shape);
 

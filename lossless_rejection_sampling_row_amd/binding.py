@@ -54,6 +54,9 @@ def load_library():
              c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]
     lib.sv_verify_batch_sched.argtypes = sched
     lib.sv_verify_batch_sched.restype = c_int
+    lib.sv_row_acceptance.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
+    lib.sv_row_acceptance.restype = c_int
     lib.sv_workspace_bytes.argtypes = [SvShape]
     lib.sv_workspace_bytes.restype = c_size_t
     lib.sv_status_string.argtypes = [c_int]
@@ -186,6 +189,50 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
         _check(lib.sv_verify_batch_diag(*args, _ptr(row_diag) if row_diag is not None else None,
                                         _ptr(stats) if stats is not None else None, ev))
     return out_tokens, out_accept_len
+
+
+def row_acceptance(target, draft, draft_tokens, row_offsets, temperature, tau, *, tau_step=None, min_cum=None,
+                   out_sum_min=None, out_sum_pq=None, workspace=None, stream=None):
+    """Per-row sum min(p, mu) and sum p q of a verify batch (sv_row_acceptance).
+
+    Arguments as for verify_batch. Returns (sum_min [R] float32, sum_pq [R] float32), NaN on
+    rows that are not proposal rows. Work is enqueued and not synchronised.
+    """
+    import torch
+    lib = load_library()
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU")
+    if draft.dtype != target.dtype or draft.shape != target.shape or target.dim() != 2:
+        raise ValueError("target and draft must be [R, V] tensors of one dtype")
+    if not (target.is_contiguous() and draft.is_contiguous()):
+        raise ValueError("logits must be contiguous")
+    R, V = int(target.shape[0]), int(target.shape[1])
+    B = int(row_offsets.numel()) - 1
+    checks = [("draft_tokens", draft_tokens, torch.int32, R), ("row_offsets", row_offsets, torch.int32, B + 1),
+              ("temperature", temperature, torch.float32, B), ("tau", tau, torch.float32, B)]
+    if tau_step is not None:
+        checks.append(("tau_step", tau_step, torch.float32, R))
+    if min_cum is not None:
+        checks.append(("min_cum", min_cum, torch.float32, B))
+    for name, t, dt, n in checks:
+        if t.dtype != dt or t.numel() != n or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {dt} [{n}] on {dev}")
+    shape = SvShape(B, R, V, dtype_code(target.dtype))
+    if out_sum_min is None:
+        out_sum_min = torch.empty(R, dtype=torch.float32, device=dev)
+    if out_sum_pq is None:
+        out_sum_pq = torch.empty(R, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(lib.sv_row_acceptance(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets),
+                                 _ptr(temperature), _ptr(tau), _ptr(tau_step) if tau_step is not None else None,
+                                 _ptr(min_cum) if min_cum is not None else None, _ptr(out_sum_min),
+                                 _ptr(out_sum_pq), shape, _ptr(workspace), c_size_t(workspace.numel()),
+                                 c_void_p(stream.cuda_stream)))
+    return out_sum_min, out_sum_pq
 
 
 def expand_schedule(schedule, row_offsets):

@@ -43,8 +43,14 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   off += (size_t)q.R * q.w1max * sizeof(P1Part);
   q.off_part2 = off = align_up(off, 256);
   off += (size_t)q.B * q.w2max * sizeof(P2Part);
+  q.off_part3 = off = align_up(off, 256);
+  off += (size_t)q.R * q.w1max * sizeof(SumPart);
+  // Counters that every call leaves at zero: pass 2's request tickets, then the acceptance
+  // sums' per-row done flags.
   q.off_ticket2 = off = align_up(off, 256);
   off += (size_t)q.B * sizeof(uint32_t);
+  q.off_done3 = off;
+  off += (size_t)q.R * sizeof(uint32_t);
   q.total = align_up(off, 256);
   *p = q;
   return SV_OK;
@@ -71,8 +77,8 @@ Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2) {
 
 sv_status check_call(const sv_shape& shape, const void* target, const void* draft,
                      const int32_t* draft_tokens, const int32_t* row_offsets,
-                     const float* temperature, const float* tau, const int32_t* out_tokens,
-                     const int32_t* out_accept_len, const void* workspace,
+                     const float* temperature, const float* tau, const void* out_tokens,
+                     const void* out_accept_len, const void* workspace,
                      size_t workspace_bytes, Plan* plan) {
   const sv_status st = make_plan(shape, plan);
   if (st != SV_OK) return st;

@@ -56,6 +56,8 @@ struct Work {
   P1Part* part1;
   P2Part* part2;
   uint32_t* t2;  // pass 2: waves finished per request
+  SumPart* part3;   // acceptance sums: one partial per (row, wave)
+  uint32_t* done3;  // acceptance sums: rows that hold partials (reset by the merge)
 };
 
 struct Outputs {
@@ -1189,6 +1191,141 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   emit_request(in, w, out, b, q, invalid, token, resid, lane);
 }
 
+// ====================================================================== acceptance sums
+
+// Per proposal row r (row j of request b): sum_x min(p(x), mu(x)), the probability that the
+// row accepts its draft given its prefix (Strata PR #3416, section Approach; mlxcel PR #992,
+// section The acceptance ceiling), and sum_x p(x) q(x), the sampler-match rule's. mu is
+// gated at the row's threshold: its step threshold raised by the cumulative floor over the
+// drafted tokens before it (regolith audit, section schedule behavior).
+//
+// The grid and the row of each wave are pass 1's. A wave first evaluates rows lo .. r from
+// pass 1's partials exactly as the walk does (eval_rows), in chunks of 64 / w1 rows: that
+// gives row r's statistics and gate threshold, and whether every row up to r is valid. It
+// then streams its span of row r and writes one partial; merge_sums_kernel adds the w1
+// partials of each row in order. A row with an invalid row up to it gets NaN.
+template <typename E, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void sums_kernel(Inputs in, Work w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int np = in.R - in.B;
+  if (gw >= (int64_t)np * in.w1) return;
+  if (!w.hdr->ro_valid) return;
+  const int p = (int)(gw / in.w1);
+  const int g = (int)(gw % in.w1);
+  const RowCls cls = classify_slot(in, p, slot_guess(in, p), lane);
+  if (!cls.proposal) return;
+  const int r = cls.r, b = cls.b, lo = cls.lo, j = cls.j;
+  const float T = cls.T, c = fold_scale(T);
+  const float floor = in.min_cum != nullptr ? in.min_cum[b] : 0.0f;
+  const bool floor_ok = __builtin_isfinite(floor) && floor >= 0.0f;
+
+  const int nw = in.w1;
+  const int per = kWave / nw;  // rows per chunk
+  double carry = 1.0;
+  bool ok = floor_ok;
+  RowStat cur{};
+  float tau_cur = 0.0f;
+  for (int base = 0; base <= j; base += per) {
+    const int ri = base + (int)(lane / nw);
+    const bool live = ri <= j;
+    const int rr = lo + min(ri, j);
+    const P1Part e = w.part1[(int64_t)rr * nw + (lane & (nw - 1))];
+    const int Di = in.dt[rr];
+    const float tsi = in.tau_step != nullptr ? in.tau_step[rr] : cls.tau;
+    const int nlive = min(per, j + 1 - base);
+    RowStat rs;
+    const RowEval ev = eval_rows<true>(in, e, live, nw, b, min(ri, j), Di, T, tsi, floor_ok ? floor : 0.0f, carry,
+                                       nlive, c, rs);
+    ok = ok && __ballot(live && ev.verdict == kRowInvalid) == 0;
+    if (base + per > j) {  // the chunk that holds row r
+      const int src = (j - base) * nw;
+      cur = RowStat{lane_of(rs.m_t, src), lane_of(rs.mc_t, src), lane_of(rs.m_d, src), lane_of(rs.mc_d, src),
+                    lane_of(rs.s_t, src), lane_of(rs.s_d, src), lane_of(rs.am_t, src), lane_of(rs.am_d, src)};
+      tau_cur = lane_of(ev.tau_eff, src);
+    }
+  }
+
+  double smin = 0.0, spq = 0.0;
+  if (!ok) {
+    smin = spq = NAN;
+  } else if (T == 0.0f) {  // one-hot p and q: both sums are [argmax p == argmax q] (the first also needs tau <= 1)
+    if (g == 0) {
+      smin = (cur.am_t == cur.am_d && 1.0f >= tau_cur) ? 1.0 : 0.0;
+      spq = cur.am_t == cur.am_d ? 1.0 : 0.0;
+    }
+  } else {
+    using CH = Chunk<E, VEC>;
+    const int nvec = in.V / VEC;
+    const Span sp = wave_span(nvec, nw, g);
+    const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
+    const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
+    const float mct = cur.mc_t, mcd = cur.mc_d, tau = tau_cur;
+    const float ist = (float)(1.0 / cur.s_t), isd = (float)(1.0 / cur.s_d);
+    constexpr int step = U * kWave;
+    float am = 0.0f, apq = 0.0f;
+    CH ta[U], da[U], tb[U], db[U];
+    auto fold = [&](const CH (&xt)[U], const CH (&xd)[U]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float pp = fast_exp2(fmaf(xt[u].get(e), c, -mct)) * ist;
+          const float qq = fast_exp2(fmaf(xd[u].get(e), c, -mcd)) * isd;
+          am += fminf(pp, qq >= tau ? qq : 0.0f);
+          apq = fmaf(pp, qq, apq);
+        }
+      }
+    };
+    const int nsteps = (sp.end - sp.begin + step - 1) / step;
+    if (nsteps > 0) {
+      load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
+      load_chunks<true>(da, drow, sp.begin, lane, sp.end);
+    }
+    for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+      load_chunks<true>(tb, trow, base + step, lane, sp.end);
+      load_chunks<true>(db, drow, base + step, lane, sp.end);
+      mask_chunks(ta, base, lane, sp.end);
+      mask_chunks(da, base, lane, sp.end);
+      fold(ta, da);
+      load_chunks<true>(ta, trow, base + 2 * step, lane, sp.end);
+      load_chunks<true>(da, drow, base + 2 * step, lane, sp.end);
+      mask_chunks(tb, base + step, lane, sp.end);
+      mask_chunks(db, base + step, lane, sp.end);
+      fold(tb, db);
+    }
+    smin = wave_sum((double)am);
+    spq = wave_sum((double)apq);
+  }
+  if (lane == 0) {
+    w.part3[(int64_t)r * nw + g] = SumPart{smin, spq};
+    if (g == 0) w.done3[r] = 1u;
+  }
+}
+
+// Adds each row's w1 partials in wave order. Rows without partials get NaN. Every done flag
+// is reset for the next call.
+__global__ __launch_bounds__(kBlock) void merge_sums_kernel(Inputs in, Work w, float* out_min, float* out_pq) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x; r < in.R; r += stride) {
+    float m = NAN, pq = NAN;
+    if (w.done3[r] != 0u) {
+      double sm = 0.0, sp = 0.0;
+      for (int g = 0; g < in.w1; ++g) {
+        const SumPart s = w.part3[r * in.w1 + g];
+        sm += s.smin;
+        sp += s.spq;
+      }
+      m = (float)sm;
+      pq = (float)sp;
+      w.done3[r] = 0u;
+    }
+    out_min[r] = m;
+    out_pq[r] = pq;
+  }
+}
+
 // ====================================================================== launch
 
 // Zero the request tickets. Every ticket wraps back to zero when a call completes, so this
@@ -1294,6 +1431,28 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   return hipSuccess;
 }
 
+template <typename E, int VEC>
+hipError_t launch_sums(const Plan& p, Inputs in, const Work& w, float* out_min, float* out_pq, hipStream_t stream) {
+  constexpr int U1 = VEC == 1 ? 8 : 2;
+  const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
+  int64_t slots1 = 0;
+  hipError_t err = resident_waves(k1, kTargetWavesPerCU, &slots1);
+  if (err != hipSuccess) return err;
+  const Launch l = pick_waves(p, slots1, slots1);
+  in.w1 = l.w1;
+  in.w2 = l.w2;
+  const Outputs none{nullptr, nullptr, nullptr, nullptr};
+  const dim3 block(kBlock);
+  hipLaunchKernelGGL((pass1_kernel<E, VEC, U1>), dim3((unsigned)l.blocks1), block, 0, stream, in, w, none);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL((sums_kernel<E, VEC, U1>), dim3((unsigned)l.blocks1), block, 0, stream, in, w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t mb = ((int64_t)p.R + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(merge_sums_kernel, dim3((unsigned)(mb < 1024 ? mb : 1024)), block, 0, stream, in, w, out_min,
+                     out_pq);
+  return hipGetLastError();
+}
+
 static sv_status run(const void* target, const void* draft, const int32_t* draft_tokens,
                      const int32_t* row_offsets, const float* temperature, const float* tau,
                      const float* tau_step, const float* min_cum,
@@ -1309,7 +1468,8 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
   Inputs in{target, draft, draft_tokens, row_offsets, temperature, tau, tau_step, min_cum,
             seed, p.B, p.R, p.V, p.dtype, 1, 1};
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
-         reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2)};
+         reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
+         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3)};
   Outputs out{out_tokens, out_accept_len, diag, stats};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
@@ -1351,6 +1511,38 @@ extern "C" sv_status sv_verify_batch_diag(const void* target_logits, const void*
   return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, nullptr, nullptr,
                  seed, out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
                  out_row_diag, out_stats, hip_events);
+}
+
+extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* draft_logits,
+                                       const int32_t* draft_tokens, const int32_t* row_offsets,
+                                       const float* temperature, const float* tau, const float* tau_step,
+                                       const float* min_cum, float* out_sum_min, float* out_sum_pq, sv_shape shape,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  using namespace sv;
+  Plan p;
+  const sv_status st = check_call(shape, target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau,
+                                  out_sum_min, out_sum_pq, workspace, workspace_bytes, &p);
+  if (st != SV_OK) return st;
+  if (shape.B == 0) return SV_OK;
+  char* ws = static_cast<char*>(workspace);
+  Inputs in{target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, tau_step, min_cum,
+            0, p.B, p.R, p.V, p.dtype, 1, 1};
+  Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
+         reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
+         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3)};
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;
+  hipError_t err = counters_ready(p, ws, stream);
+  if (err != hipSuccess) return SV_E_HIP;
+  if (p.dtype == SV_BF16) {
+    err = aligned ? launch_sums<uint16_t, 8>(p, in, w, out_sum_min, out_sum_pq, stream)
+                  : launch_sums<uint16_t, 1>(p, in, w, out_sum_min, out_sum_pq, stream);
+  } else {
+    err = aligned ? launch_sums<float, 4>(p, in, w, out_sum_min, out_sum_pq, stream)
+                  : launch_sums<float, 1>(p, in, w, out_sum_min, out_sum_pq, stream);
+  }
+  return err == hipSuccess ? SV_OK : SV_E_HIP;
 }
 
 extern "C" sv_status sv_verify_batch_sched(const void* target_logits, const void* draft_logits,

@@ -69,6 +69,12 @@ struct P2Part {
 };
 static_assert(sizeof(P2Part) == 32, "P2Part layout");
 
+// Acceptance sums: one partial per (row, pass-1 wave) of sum min(p, mu) and sum p q.
+struct SumPart {
+  double smin, spq;
+};
+static_assert(sizeof(SumPart) == 16, "SumPart layout");
+
 struct WsHeader {
   int32_t ro_valid;  // row_offsets check result, written by pass 1
   int32_t pad[63];
@@ -80,7 +86,7 @@ struct Plan {
   int32_t esize;  // bytes per logit
   int32_t w1max;  // pass 1: most waves that share one row (sizes the partial array)
   int32_t w2max;  // pass 2: most waves that share one request
-  size_t off_hdr, off_part1, off_part2, off_ticket2, total;
+  size_t off_hdr, off_part1, off_part2, off_part3, off_ticket2, off_done3, total;
 };
 
 // Build the plan for a shape. Returns SV_OK, or the status describing why the
@@ -98,11 +104,12 @@ struct Launch {
 // resident: one round of waves covers the work, and no split exceeds the plan's bounds.
 Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2);
 
-// Validate every host-checkable argument of a verify call.
+// Validate every host-checkable argument of a verify call. The two outputs are only
+// null-checked (the acceptance sums pass their two float arrays).
 sv_status check_call(const sv_shape& shape, const void* target, const void* draft,
                      const int32_t* draft_tokens, const int32_t* row_offsets,
-                     const float* temperature, const float* tau, const int32_t* out_tokens,
-                     const int32_t* out_accept_len, const void* workspace,
+                     const float* temperature, const float* tau, const void* out_tokens,
+                     const void* out_accept_len, const void* workspace,
                      size_t workspace_bytes, Plan* plan);
 
 }  // namespace sv

@@ -421,6 +421,10 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
     row without a proposal and before its last row; every other row gets NaN.
     A request that ``verify_request`` would fail closed on its knobs, or a row
     whose logits are invalid, gets NaN.
+
+    Returns (sum_min, sum_pq, near_gate): near_gate[r] marks a row with some
+    |q(x) - tau_j| < FLAG_EPS (tau_j > 0), where a float32 gate decision may
+    legitimately differ.
     """
     target = np.asarray(target)
     R, V = target.shape
@@ -428,8 +432,9 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
     B = ro.size - 1
     smin = np.full(R, np.nan)
     spq = np.full(R, np.nan)
+    near = np.zeros(R, dtype=bool)
     if not row_offsets_valid(ro, R):
-        return smin, spq
+        return smin, spq, near
     temperature = np.asarray(temperature, dtype=np.float32).astype(np.float64)
     tau = np.asarray(tau, dtype=np.float32).astype(np.float64)
     dt = np.asarray(draft_tokens, dtype=np.int64)
@@ -460,5 +465,6 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
                 tau_j = max(tau_j, floor / cum)
             smin[r] = acceptance_probability(p, retained_measure(q, tau_j))
             spq[r] = sum_prod(p, q)
+            near[r] = tau_j > 0.0 and bool((np.abs(q - tau_j) < FLAG_EPS).any())
             cum *= q[D]
-    return smin, spq
+    return smin, spq, near

@@ -26,8 +26,9 @@ def _logits(law):
 
 def _sums(rows_t, rows_d, dt, T, tau, **kw):
     b = batch_from_rows(rows_t, rows_d, dt, [0, len(dt)], [T], [tau])
-    return ov.row_sums(b["target"], b["draft"], b["draft_tokens"], b["row_offsets"], b["temperature"],
-                       b["tau"], "f32", **kw)
+    smin, spq, _ = ov.row_sums(b["target"], b["draft"], b["draft_tokens"], b["row_offsets"], b["temperature"],
+                               b["tau"], "f32", **kw)
+    return smin, spq
 
 
 def test_matches_exact_closed_form():

@@ -163,6 +163,61 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(rec))
 
 
+def bench_row_sums(args, binding, torch, sets, ws, stream):
+    """K calls of sv_row_acceptance over the rotating input sets. The two-pass method reads every
+    proposal row twice (statistics, then the sums), so its algorithmic bytes are twice pass 1's."""
+    from lossless_rejection_sampling_row_amd import workloads as wl
+    K, W = args.steps, args.warmup
+    nsets = len(sets)
+    w0 = sets[0][0]
+    R, V = w0.R, w0.V
+    esize = 2 if w0.dtype == "bf16" else 4
+    smin = torch.empty(R, dtype=torch.float32, device=stream.device)
+    spq = torch.empty(R, dtype=torch.float32, device=stream.device)
+
+    def call(i):
+        _, g = sets[i % nsets]
+        binding.row_acceptance(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"], g["temperature"],
+                               g["tau"], out_sum_min=smin, out_sum_pq=spq, workspace=ws, stream=stream)
+
+    for i in range(W):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        call(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    prop = np.array([proposal_rows(sets[i % nsets][0]) for i in range(K)], dtype=np.float64)
+    alg = 2.0 * prop * V * 2 * esize
+    gbps = alg.mean() / (ms / 1e3) / 1e9
+    log(f"[bench] row sums: {ms * 1e3:.1f} us/call, {gbps:.0f} GB/s of algorithmic bytes")
+    line = {
+        "metric": "per-row acceptance sums (sum min(p, mu), sum p q): rows/s and algorithmic GB/s",
+        "value": round(R / (ms / 1e3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.CONFIG_NAMES[args.config], "rows": R, "V": V, "logits": w0.dtype,
+                   "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "pass1_kernel + sums_kernel + merge_sums_kernel (one call)",
+                     "launch_us": round(ms * 1e3, 2), "alg_bytes_per_launch": int(alg.mean())},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +229,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the steps, copy a MIB-MiB device buffer three times (a plain copy of known size "
                          "whose FETCH_SIZE / WRITE_SIZE scale the counters of the verify kernels)")
+    ap.add_argument("--row-sums", action="store_true",
+                    help="time the per-row acceptance sums (sv_row_acceptance) on the same inputs instead of the "
+                         "verify call, and print their own JSON line")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE runs "
                          "with --copy-calibration) into the traffic record the roofline entry reads")
@@ -221,8 +279,11 @@ def main():
     out_len = torch.empty((K, B), dtype=torch.int32, device=dev)
     scratch_tok = torch.empty(R, dtype=torch.int32, device=dev)
     scratch_len = torch.empty(B, dtype=torch.int32, device=dev)
-    ev = binding.HipEvents(3 * K)
     stream = torch.cuda.current_stream(dev)
+    if args.row_sums:
+        bench_row_sums(args, binding, torch, sets, ws, stream)
+        return
+    ev = binding.HipEvents(3 * K)
 
     def step(i, timed, events=False):
         w, g = sets[i % nsets]

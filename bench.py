@@ -82,6 +82,25 @@ def pass2_bytes(w, accept_len: np.ndarray, esize: int) -> int:
     return tot
 
 
+def tested_rows(w, accept_len: np.ndarray) -> int:
+    """Rows the lazy verify streams: each request's rows up to its stop (the stop row included
+    when it is a proposal row), as given by its accept length."""
+    ro, dt, V = w.row_offsets, w.draft_tokens, w.V
+    n = 0
+    for b in range(w.B):
+        k = int(accept_len[b])
+        if k < 0:
+            continue
+        lo, hi = int(ro[b]), int(ro[b + 1])
+        nprop = 0
+        for r in range(lo, hi - 1):
+            if not (0 <= dt[r] < V):
+                break
+            nprop += 1
+        n += min(k + 1, nprop)
+    return n
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the oracle as it stands on one process over whole batches of this workload."""
     from oracle import verify as ov
@@ -163,6 +182,67 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(rec))
 
 
+def bench_lazy(args, binding, torch, sets, ws, stream):
+    """K lazy verify calls over the rotating input sets. Algorithmic bytes: the rows each request
+    must read up to its stop, its final row's bytes, and the small arrays."""
+    from lossless_rejection_sampling_row_amd import workloads as wl
+    K, W = args.steps, args.warmup
+    nsets = len(sets)
+    w0 = sets[0][0]
+    B, R, V = w0.B, w0.R, w0.V
+    esize = 2 if w0.dtype == "bf16" else 4
+    max_rows = int(np.diff(w0.row_offsets).max())
+    out_tok = torch.empty((K, R), dtype=torch.int32, device=stream.device)
+    out_len = torch.empty((K, B), dtype=torch.int32, device=stream.device)
+
+    def call(i, tok, ln):
+        _, g = sets[i % nsets]
+        binding.verify_batch(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"], g["temperature"],
+                             g["tau"], 1_000_003 * i + 17, out_tokens=tok, out_accept_len=ln, workspace=ws,
+                             stream=stream, lazy_max_rows=max_rows)
+
+    for i in range(W):
+        call(i, out_tok[0], out_len[0])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        call(i, out_tok[i], out_len[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    lens = out_len.cpu().numpy()
+    alg = np.array([tested_rows(sets[i % nsets][0], lens[i]) * V * 2 * esize
+                    + pass2_bytes(sets[i % nsets][0], lens[i], esize) + 16 * R + 8 * B for i in range(K)],
+                   dtype=np.float64)
+    rows_read = np.mean([tested_rows(sets[i % nsets][0], lens[i]) for i in range(K)])
+    gbps = alg.mean() / (ms / 1e3) / 1e9
+    log(f"[bench] lazy: {ms * 1e3:.1f} us/step, {rows_read:.1f} of {proposal_rows(w0)} proposal rows read, "
+        f"{gbps:.0f} GB/s of algorithmic bytes")
+    line = {
+        "metric": "verified rows/sec, lazy position-serial verify (reads rows up to each request's first rejection)",
+        "value": round(R / (ms / 1e3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.CONFIG_NAMES[args.config], "B": B, "rows": R, "V": V, "logits": w0.dtype,
+                   "input_sets": nsets, "max_rows": max_rows, "rows_read_per_step": round(float(rows_read), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"{max(1, max_rows - 1)} x lazy_rows_kernel + pass2_kernel (one call)",
+                     "launch_us": round(ms * 1e3, 2), "alg_bytes_per_launch": int(alg.mean())},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_row_sums(args, binding, torch, sets, ws, stream):
     """K calls of sv_row_acceptance over the rotating input sets. The two-pass method reads every
     proposal row twice (statistics, then the sums), so its algorithmic bytes are twice pass 1's."""
@@ -232,6 +312,9 @@ def main():
     ap.add_argument("--row-sums", action="store_true",
                     help="time the per-row acceptance sums (sv_row_acceptance) on the same inputs instead of the "
                          "verify call, and print their own JSON line")
+    ap.add_argument("--lazy", action="store_true",
+                    help="time the lazy position-serial verify (sv_verify_batch_lazy) instead, and print its own "
+                         "JSON line; its algorithmic bytes count only the rows it must read")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE runs "
                          "with --copy-calibration) into the traffic record the roofline entry reads")
@@ -282,6 +365,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.row_sums:
         bench_row_sums(args, binding, torch, sets, ws, stream)
+        return
+    if args.lazy:
+        bench_lazy(args, binding, torch, sets, ws, stream)
         return
     ev = binding.HipEvents(3 * K)
 

@@ -219,6 +219,28 @@ sv_status sv_verify_batch_sched(const void* target_logits, const void* draft_log
                                 sv_batch_stats* out_stats);
 
 /*
+ * sv_verify_batch_lazy - sv_verify_batch, reading rows only up to each
+ * request's first row that is not accepted.
+ *
+ * Same arguments, results, ownership, workspace and errors as
+ * sv_verify_batch; the outputs are identical. max_rows bounds the rows of
+ * every request (typically the number of draft positions plus one). Position j
+ * of all requests is verified by launch j, max(1, max_rows - 1) launches in
+ * all, so the call trades that many dependent launches for bytes: a request
+ * whose draft at position j is rejected never has rows j+1... read. mlxcel
+ * PR #992, section Two metric corrections: the positions behind the first
+ * rejection are never tested. A batch with a request of more than max_rows
+ * rows fails closed like broken row_offsets (every output -1).
+ * max_rows   1 .. 4096, else SV_E_SHAPE.
+ */
+sv_status sv_verify_batch_lazy(const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_tokens, const int32_t* row_offsets,
+                               const float* temperature, const float* tau, uint64_t seed,
+                               int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
+                               void* workspace, size_t workspace_bytes, void* hip_stream,
+                               int32_t max_rows);
+
+/*
  * sv_row_acceptance - per-row acceptance sums of a verify batch.
  *
  * For every proposal row r (row j of request b; the rows before a request's

@@ -57,6 +57,8 @@ def load_library():
     lib.sv_row_acceptance.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
     lib.sv_row_acceptance.restype = c_int
+    lib.sv_verify_batch_lazy.argtypes = common + [c_int]
+    lib.sv_verify_batch_lazy.restype = c_int
     lib.sv_workspace_bytes.argtypes = [SvShape]
     lib.sv_workspace_bytes.restype = c_size_t
     lib.sv_status_string.argtypes = [c_int]
@@ -112,7 +114,7 @@ def _ptr(t):
 
 def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int, *,
                  out_tokens=None, out_accept_len=None, workspace=None, row_diag=None, stats=None,
-                 events=None, stream=None, tau_step=None, min_cum=None):
+                 events=None, stream=None, tau_step=None, min_cum=None, lazy_max_rows=None):
     """Verify a batch of speculative windows on the GPU.
 
     target, draft : [R, V] bfloat16 or float32 (same dtype), row-major, on one GPU.
@@ -127,6 +129,8 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     tau_step      : optional [R] float32 per-row gate thresholds (see expand_schedule).
     min_cum       : optional [B] float32 cumulative floors (0 = off).
     With tau_step or min_cum the call goes to sv_verify_batch_sched (no events).
+    lazy_max_rows : with a bound on every request's rows, the call goes to sv_verify_batch_lazy,
+                    which reads rows only up to each request's first rejection (plain outputs only).
     stream        : optional torch stream (default: the current stream).
 
     Returns (out_tokens [R] int32, out_accept_len [B] int32). Work is enqueued
@@ -173,7 +177,11 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
         raise ValueError("row_diag must be an int32 tensor with 8*R elements")
     if stats is not None and (stats.dtype != torch.int64 or stats.numel() != 8):
         raise ValueError("stats must be an int64 tensor with 8 elements")
-    if tau_step is not None or min_cum is not None:
+    if lazy_max_rows is not None:
+        if any(x is not None for x in (row_diag, stats, events, tau_step, min_cum)):
+            raise ValueError("the lazy verify has plain outputs only")
+        _check(lib.sv_verify_batch_lazy(*args, c_int(int(lazy_max_rows))))
+    elif tau_step is not None or min_cum is not None:
         if events is not None:
             raise ValueError("events are not supported together with tau_step / min_cum")
         sargs = args[:6] + [_ptr(tau_step) if tau_step is not None else None,

@@ -58,6 +58,7 @@ struct Work {
   uint32_t* t2;  // pass 2: waves finished per request
   SumPart* part3;   // acceptance sums: one partial per (row, wave)
   uint32_t* done3;  // acceptance sums: rows that hold partials (reset by the merge)
+  int32_t* lazy_stop;  // lazy verify: the request's window has stopped
 };
 
 struct Outputs {
@@ -307,14 +308,16 @@ __device__ __forceinline__ void wave_stat(const Acc& a, float c, bool sums, floa
   }
 }
 
-// Block 0 checks row_offsets for the whole batch and clears the stats.
-__device__ void block0_duties(const Inputs& in, const Work& w, const Outputs& out) {
+// Block 0 checks row_offsets for the whole batch and clears the stats. With max_rows > 0 a
+// request of more rows than that also fails the batch (the lazy verify streams only that many).
+__device__ void block0_duties(const Inputs& in, const Work& w, const Outputs& out, int max_rows = 0) {
   __shared__ int s_bad;
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
   int bad = 0;
   if (threadIdx.x == 0) bad = (in.ro[0] != 0) || (in.ro[in.B] != in.R);
-  for (int i = threadIdx.x; i < in.B; i += kBlock) bad |= !(in.ro[i] < in.ro[i + 1]);
+  for (int i = threadIdx.x; i < in.B; i += kBlock)
+    bad |= !(in.ro[i] < in.ro[i + 1]) || (max_rows > 0 && in.ro[i + 1] - in.ro[i] > max_rows);
   if (bad) atomicOr(&s_bad, 1);
   __syncthreads();
   if (threadIdx.x == 0) w.hdr->ro_valid = s_bad ? 0 : 1;
@@ -325,49 +328,20 @@ __device__ void block0_duties(const Inputs& in, const Work& w, const Outputs& ou
 
 // Waves, not workgroups, are assigned to slots: wave gw of the grid streams span gw % w1 of
 // slot gw / w1, so the split need not be a multiple of a workgroup's four waves.
+// Stream span sp of proposal row r, both arrays, and write the wave's partial at slot g of
+// the row. ta / da already hold the span's first batch (requested by the caller, so that it
+// travels with the caller's own round trips).
 template <typename E, int VEC, int U>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void pass1_kernel(Inputs in, Work w,
-                                                                                             Outputs out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (blockIdx.x == 0) block0_duties(in, w, out);
-  const int np = in.R - in.B;
-  if (gw >= (int64_t)np * in.w1) return;
-  const int p = (int)(gw / in.w1);
-  const int g = (int)(gw % in.w1);
-
+__device__ __forceinline__ void stream_span(const Inputs& in, const Work& w, int r, int g, float T, int D,
+                                            const E* trow, const E* drow, Span sp, Chunk<E, VEC> (&ta)[U],
+                                            Chunk<E, VEC> (&da)[U], int lane) {
   using CH = Chunk<E, VEC>;
-  const int nvec = in.V / VEC;
-  const Span sp = wave_span(nvec, in.w1, g);
-  const int bg = slot_guess(in, p);
-  const int rg = min(p + bg, in.R - 1);
-  const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)rg * in.V;
-  const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)rg * in.V;
   constexpr int step = U * kWave;
-  CH ta[U], da[U], tb[U], db[U];
-  // The first batch of the guessed row is requested before the slot is classified, so the
-  // row's metadata and its first logits arrive together.
-  if (sp.begin < sp.end) {
-    load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
-    load_chunks<true>(da, drow, sp.begin, lane, sp.end);
-  }
-  const RowCls cls = classify_slot(in, p, bg, lane);
-  if (!cls.proposal) return;
-  const int r = cls.r;
-  if (r != rg) {  // the guess missed: stream the right row
-    trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
-    drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
-    if (sp.begin < sp.end) {
-      load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
-      load_chunks<true>(da, drow, sp.begin, lane, sp.end);
-    }
-  }
-
-  const bool greedy = cls.T == 0.0f;
-  const float c = fold_scale(cls.T);
-  const int dvec = cls.D / VEC;
-  const int de = cls.D - dvec * VEC;
+  CH tb[U], db[U];
+  const bool greedy = T == 0.0f;
+  const float c = fold_scale(T);
+  const int dvec = D / VEC;
+  const int de = D - dvec * VEC;
   const bool holds_D = dvec >= sp.begin && dvec < sp.end;  // only this span's wave reads D's logits
 
   Acc at = acc_empty(), ad = acc_empty();
@@ -423,6 +397,47 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   pp.ld_D = lane_of(ldD, src);
   pp.flags = fm ? 2 : 0;
   if (lane == 0) w.part1[(int64_t)r * in.w1 + g] = pp;  // read by pass 2, after this kernel
+}
+
+template <typename E, int VEC, int U>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void pass1_kernel(Inputs in, Work w,
+                                                                                             Outputs out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (blockIdx.x == 0) block0_duties(in, w, out);
+  const int np = in.R - in.B;
+  if (gw >= (int64_t)np * in.w1) return;
+  const int p = (int)(gw / in.w1);
+  const int g = (int)(gw % in.w1);
+
+  using CH = Chunk<E, VEC>;
+  const int nvec = in.V / VEC;
+  const Span sp = wave_span(nvec, in.w1, g);
+  const int bg = slot_guess(in, p);
+  const int rg = min(p + bg, in.R - 1);
+  const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)rg * in.V;
+  const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)rg * in.V;
+  CH ta[U], da[U];
+  // The first batch of the guessed row is requested before the slot is classified, so the
+  // row's metadata and its first logits arrive together.
+  if (sp.begin < sp.end) {
+    load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
+    load_chunks<true>(da, drow, sp.begin, lane, sp.end);
+  }
+  const RowCls cls = classify_slot(in, p, bg, lane);
+  if (!cls.proposal) return;
+  const int r = cls.r;
+  if (r != rg) {  // the guess missed: stream the right row
+    trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
+    drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
+    if (sp.begin < sp.end) {
+      load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
+      load_chunks<true>(da, drow, sp.begin, lane, sp.end);
+    }
+  }
+
+  stream_span<E, VEC, U>(in, w, r, g, cls.T, cls.D, trow, drow, sp, ta, da, lane);
 }
 
 // ====================================================================== pass 2
@@ -845,7 +860,8 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
 // every token's p and mu, and its walk applies per-row step thresholds and the cumulative
 // floor.
 // The plain call's waves skip, by one test in the logit domain, every 16-byte vector that
-// can hold neither a race candidate nor a token that passes the gate.
+// cannot hold a race candidate: r = (p - mu)+ <= p, so a vector whose largest p is below the
+// pruning threshold holds none, whatever mu is.
 template <typename E, int VEC, int U, bool DIAG>
 __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Outputs out) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -974,14 +990,11 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     auto fold_res = [&](const CH (&xt)[U], const CH (&xd)[U], int v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (!DIAG) {
-          float mt = xt[u].get(0), md = xd[u].get(0);
+        if (!DIAG) {  // r <= p: no token of a vector whose largest p misses pthr is a candidate
+          float mt = xt[u].get(0);
 #pragma unroll
-          for (int e = 1; e < VEC; ++e) {
-            mt = fmaxf(mt, xt[u].get(e));
-            md = fmaxf(md, xd[u].get(e));
-          }
-          if (!(fmaf(mt, c, -mct) >= sthr) && !(md >= gate_l)) continue;
+          for (int e = 1; e < VEC; ++e) mt = fmaxf(mt, xt[u].get(e));
+          if (!(fmaf(mt, c, -mct) >= sthr)) continue;
         }
         const int x0 = (v0 + u * kWave) * VEC;
         float rv[VEC], mv[VEC];
@@ -1189,6 +1202,59 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     }
   }
   emit_request(in, w, out, b, q, invalid, token, resid, lane);
+}
+
+// ====================================================================== lazy verify
+
+// Position-serial verify (the survey's "lazy" row): launch j streams row j of every request
+// whose rows 0 .. j-1 were all accepted, so rows are read only up to each request's first
+// row that is not accepted. A wave of launch j first evaluates row j-1 from its pass-1
+// partials exactly as the walk does (eval_rows); a request whose row j-1 is not accepted is
+// marked stopped and streams nothing more. Pass 2 then walks and draws unchanged: the
+// partials of every row up to the stop are in place, and the rows behind it are never
+// decisive (the walk stops at the first row that is not accepted).
+template <typename E, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void lazy_rows_kernel(Inputs in, Work w, int j, int max_rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (j == 0 && blockIdx.x == 0) block0_duties(in, w, Outputs{nullptr, nullptr, nullptr, nullptr}, max_rows);
+  const int nw = in.w1;
+  if (gw >= (int64_t)in.B * nw) return;
+  const int b = (int)(gw / nw), g = (int)(gw % nw);
+  // One round trip: the request head, the drafted token and the stop flag.
+  const int lo = in.ro[b], hi = in.ro[b + 1];
+  const float T = in.temp[b], tau = in.tau[b];
+  const int stop = j > 0 ? w.lazy_stop[b] : 0;
+  if (!(0 <= lo && lo < hi && hi <= in.R)) return;  // broken row_offsets: pass 2 fails the batch
+  if (j >= hi - lo - 1) return;                      // row j is the request's last row, or beyond
+  const int r = lo + j;
+  const int D = in.dt[r];
+  if (stop != 0 || !temperature_ok(T) || __builtin_isnan(tau) || D < 0 || D >= in.V) return;
+
+  using CH = Chunk<E, VEC>;
+  const Span sp = wave_span(in.V / VEC, nw, g);
+  const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
+  const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
+  CH ta[U], da[U];
+  if (sp.begin < sp.end) {  // in flight while row j-1 is evaluated
+    load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
+    load_chunks<true>(da, drow, sp.begin, lane, sp.end);
+  }
+  if (j > 0) {
+    const P1Part e = w.part1[(int64_t)(r - 1) * nw + (lane & (nw - 1))];
+    RowStat rs;
+    double carry = 1.0;
+    const RowEval ev = eval_rows<false>(in, e, lane < nw, nw, b, j - 1, in.dt[r - 1], T, tau, 0.0f, carry, 1,
+                                        fold_scale(T), rs);
+    if (lane_of(ev.verdict, 0) != SV_ROW_ACCEPT) {
+      if (g == 0 && lane == 0) w.lazy_stop[b] = 1;
+      return;
+    }
+  } else if (g == 0 && lane == 0) {
+    w.lazy_stop[b] = 0;
+  }
+  stream_span<E, VEC, U>(in, w, r, g, T, D, trow, drow, sp, ta, da, lane);
 }
 
 // ====================================================================== acceptance sums
@@ -1432,6 +1498,32 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
 }
 
 template <typename E, int VEC>
+hipError_t launch_lazy(const Plan& p, Inputs in, const Work& w, const Outputs& out, hipStream_t stream,
+                       int max_rows) {
+  constexpr int U1 = VEC == 1 ? 8 : 2;
+  constexpr int U2 = VEC == 1 ? 8 : 2;
+  // As many waves per row as a row allows (a power of two): launch j streams few rows.
+  int nw = 1;
+  while (nw * 2 <= p.w1max) nw *= 2;
+  const void* k2 = reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, false>);
+  int64_t slots2 = 0;
+  hipError_t err = resident_waves(k2, kTargetWavesPerCU2, &slots2);
+  if (err != hipSuccess) return err;
+  const Launch l = pick_waves(p, slots2, slots2);
+  in.w1 = nw;
+  in.w2 = l.w2;
+  const dim3 block(kBlock);
+  const int64_t blocks = ((int64_t)p.B * nw + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int steps = max_rows > 1 ? max_rows - 1 : 1;  // launch 0 also checks the batch
+  for (int j = 0; j < steps; ++j) {
+    hipLaunchKernelGGL((lazy_rows_kernel<E, VEC, U1>), dim3((unsigned)blocks), block, 0, stream, in, w, j, max_rows);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, false>), dim3((unsigned)l.blocks2), block, 0, stream, in, w, out);
+  return hipGetLastError();
+}
+
+template <typename E, int VEC>
 hipError_t launch_sums(const Plan& p, Inputs in, const Work& w, float* out_min, float* out_pq, hipStream_t stream) {
   constexpr int U1 = VEC == 1 ? 8 : 2;
   const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
@@ -1469,7 +1561,8 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
             seed, p.B, p.R, p.V, p.dtype, 1, 1};
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
          reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
-         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3)};
+         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3),
+         reinterpret_cast<int32_t*>(ws + p.off_lazy)};
   Outputs out{out_tokens, out_accept_len, diag, stats};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
@@ -1513,6 +1606,42 @@ extern "C" sv_status sv_verify_batch_diag(const void* target_logits, const void*
                  out_row_diag, out_stats, hip_events);
 }
 
+extern "C" sv_status sv_verify_batch_lazy(const void* target_logits, const void* draft_logits,
+                                          const int32_t* draft_tokens, const int32_t* row_offsets,
+                                          const float* temperature, const float* tau, uint64_t seed,
+                                          int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
+                                          void* workspace, size_t workspace_bytes, void* hip_stream,
+                                          int32_t max_rows) {
+  using namespace sv;
+  Plan p;
+  const sv_status st = check_call(shape, target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau,
+                                  out_tokens, out_accept_len, workspace, workspace_bytes, &p);
+  if (st != SV_OK) return st;
+  if (shape.B == 0) return SV_OK;
+  if (max_rows < 1 || max_rows > 4096) return SV_E_SHAPE;
+  char* ws = static_cast<char*>(workspace);
+  Inputs in{target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, nullptr, nullptr,
+            seed, p.B, p.R, p.V, p.dtype, 1, 1};
+  Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
+         reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
+         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3),
+         reinterpret_cast<int32_t*>(ws + p.off_lazy)};
+  Outputs out{out_tokens, out_accept_len, nullptr, nullptr};
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;
+  hipError_t err = counters_ready(p, ws, stream);
+  if (err != hipSuccess) return SV_E_HIP;
+  if (p.dtype == SV_BF16) {
+    err = aligned ? launch_lazy<uint16_t, 8>(p, in, w, out, stream, max_rows)
+                  : launch_lazy<uint16_t, 1>(p, in, w, out, stream, max_rows);
+  } else {
+    err = aligned ? launch_lazy<float, 4>(p, in, w, out, stream, max_rows)
+                  : launch_lazy<float, 1>(p, in, w, out, stream, max_rows);
+  }
+  return err == hipSuccess ? SV_OK : SV_E_HIP;
+}
+
 extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* draft_logits,
                                        const int32_t* draft_tokens, const int32_t* row_offsets,
                                        const float* temperature, const float* tau, const float* tau_step,
@@ -1529,7 +1658,8 @@ extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* dr
             0, p.B, p.R, p.V, p.dtype, 1, 1};
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
          reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
-         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3)};
+         reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3),
+         reinterpret_cast<int32_t*>(ws + p.off_lazy)};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;

@@ -39,7 +39,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) >= {"sv_verify_batch", "sv_verify_batch_diag", "sv_verify_batch_sched", "sv_workspace_bytes",
+    assert set(names) >= {"sv_verify_batch", "sv_verify_batch_diag", "sv_verify_batch_sched", "sv_verify_batch_lazy",
+                          "sv_row_acceptance", "sv_workspace_bytes",
                           "sv_status_string", "sv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"

@@ -25,6 +25,16 @@
 //    before drawing their random numbers. It re-evaluates its two best fp32
 //    candidates in fp64.
 //  - The request's last wave (atomic ticket) merges and writes the outputs.
+//  - Two instances: the plain call's, and the diagnostic / scheduled calls',
+//    which also reports the residual mass and applies per-row gate schedules
+//    and the cumulative floor (regolith audit, section schedule behavior).
+//
+// Other entry points reuse these pieces:
+//  - the lazy verify streams row j of the still-open requests in launch j
+//    (lazy_rows_kernel), then runs pass 2;
+//  - the acceptance sums run pass 1, stream every proposal row again for
+//    sum min(p, mu) and sum p q (sums_kernel), and add the per-wave partials
+//    (merge_sums_kernel).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

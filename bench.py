@@ -43,10 +43,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and blank space are dropped first, so that an
+    edit of a comment does not void counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -31,6 +31,10 @@ float64 without rounding. Citations name the page and the section:
   q that underflowed to zero cannot admit a token with p = 0. This oracle uses
   the strict form u*mu(D) < p(D), which carries that p > 0 requirement. See
   ``_accept``.
+* mlxcel PR #992, section What changed. The sampler's filter chain
+  (temperature, top-k, top-p, min-p) defines the effective p and q. The
+  target's and the draft's filters are optional inputs per request. See
+  ``filters`` for the readings and the flag F5.
 * mlxcel PR #992, section Temperature 0. A greedy configuration turns p and q
   into one-hot argmax indicators, so no randomness decides anything.
 * mlxcel PR #992, section Two metric corrections. A chain stops at its first
@@ -64,6 +68,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import philox
+from .filters import Filter, filter_active, filter_valid, filtered_distribution
 
 # Row verdicts (also the codes the GPU side reports in its row diagnostics).
 ACCEPT, REJECT, NULL, BONUS = 1, 2, 3, 4
@@ -78,6 +83,7 @@ F_ACCEPT = 1      # F1: the accept uniform is near p(D)/mu(D)
 F_GATE = 2        # F2: q(D) is near tau
 F_RACE = 4        # F3: the two best race keys are near each other
 F_SUPPORT = 8     # F4: some q_x is near tau, or the residual mass is near 0, in a residual race
+F_FILTER = 16     # F5: a top-p or min-p decision of an evaluated row is near its boundary
 
 
 # ---------------------------------------------------------------- decoding
@@ -125,6 +131,17 @@ def distribution(logits: np.ndarray, T: float) -> np.ndarray:
         out[argmax_lowest(logits)] = 1.0
         return out
     return softmax(logits, T)
+
+
+def row_distribution(logits: np.ndarray, T: float, filt: Filter | None):
+    """(p, near): ``distribution`` with the sampler's filter chain applied when T > 0.
+
+    The filters follow mlxcel PR #992, section What changed (see ``filters``).
+    ``near`` flags a filter decision within its band.
+    """
+    if T > 0.0 and filt is not None and filter_active(filt, logits.size):
+        return filtered_distribution(logits, T, filt)
+    return distribution(logits, T), False
 
 
 def retained_measure(q: np.ndarray, tau: float) -> np.ndarray:
@@ -178,7 +195,8 @@ def _top2_gap(keys: np.ndarray, cond: np.ndarray | None):
 
 def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau: float,
                    seed: int, b: int, rule: str = "mu", tau_steps: np.ndarray | None = None,
-                   min_cum: float = 0.0) -> RequestResult:
+                   min_cum: float = 0.0, tfilt: Filter | None = None,
+                   dfilt: Filter | None = None) -> RequestResult:
     """Verify one request's window of rows.
 
     ``tl``, ``dl`` are float64 [n, V] target and draft logits, and ``dt`` is
@@ -189,6 +207,11 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
     replaces ``tau`` for that row. ``min_cum`` is the cumulative floor (0 turns
     that gate off). Row j gates at tau_j = max(step threshold, min_cum / the
     product of q_i(D_i) over the accepted rows i < j).
+
+    ``tfilt`` and ``dfilt`` are the target's and the draft's filter chains
+    (top-k, top-p, min-p; mlxcel PR #992, section What changed). When T > 0,
+    p and q are the filtered distributions, and an invalid filter makes the
+    request invalid. A greedy request ignores both.
 
     ``rule`` selects the method ("mu") or a deliberately wrong rule that the
     pages use as a negative control:
@@ -216,10 +239,14 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
       and mu moves the key r/E.
     * F4: a residual race with some |q_x - tau_j| < eps (tau_j > 0), or a
       residual mass below eps.
+    * F5: a filter decision near its boundary on a row the method evaluates
+      (``filters.threshold``).
     """
     n, V = tl.shape
     res = RequestResult(tokens=[], accept_len=-1)
     if not temperature_valid(T) or np.isnan(tau) or not (np.isfinite(min_cum) and min_cum >= 0.0):
+        return res
+    if T > 0.0 and any(f is not None and not filter_valid(f) for f in (tfilt, dfilt)):
         return res
     cum = 1.0  # product of q_i(D_i) over the accepted rows so far
     for j in range(n):
@@ -229,7 +256,9 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
             res.tokens = []
             res.rows.append(RowRecord(j=j, verdict=0))
             return res
-        p = distribution(tl[j], T)
+        p, near = row_distribution(tl[j], T, tfilt)
+        if near and rule == "mu":
+            res.flags |= F_FILTER
         if bonus:
             E = philox.race_exponentials(seed, b, j, V)
             tok = race(p, E)
@@ -245,7 +274,9 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
             res.tokens = []
             res.rows.append(RowRecord(j=j, verdict=0))
             return res
-        q = distribution(dl[j], T)
+        q, near = row_distribution(dl[j], T, dfilt)
+        if near and rule == "mu":
+            res.flags |= F_FILTER
         rec = RowRecord(j=j, verdict=0, p_D=float(p[D]), q_D=float(q[D]))
         tau_j = tau if tau_steps is None else float(tau_steps[j])
         if np.isnan(tau_j):
@@ -346,15 +377,28 @@ class BatchResult:
     resid_mass: np.ndarray      # [R] float64, set on residual rows only
 
 
+def request_filter(triple, b: int) -> Filter | None:
+    """Request b's filter from a (top_k, top_p, min_p) triple of [B] arrays (None: off)."""
+    if triple is None:
+        return None
+    k, tp, mp = triple
+    return Filter(top_k=0 if k is None else int(np.asarray(k, dtype=np.int32)[b]),
+                  top_p=1.0 if tp is None else float(np.asarray(tp, dtype=np.float32)[b]),
+                  min_p=0.0 if mp is None else float(np.asarray(mp, dtype=np.float32)[b]))
+
+
 def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int,
-                 dtype: str, requests=None, rule: str = "mu", tau_step=None, min_cum=None) -> BatchResult:
+                 dtype: str, requests=None, rule: str = "mu", tau_step=None, min_cum=None,
+                 target_filter=None, draft_filter=None) -> BatchResult:
     """Verify every request of a batch (or only those listed in ``requests``).
 
     ``target`` and ``draft`` are [R, V] arrays of bf16 bit patterns (uint16) or
     fp32 values. The other arguments mirror the C-ABI entry point. Requests not
     in ``requests`` keep -1 outputs. ``tau_step`` ([R] float32) and ``min_cum``
     ([B] float32) are the optional per-row step thresholds and per-request
-    cumulative floors.
+    cumulative floors. ``target_filter`` and ``draft_filter`` are optional
+    triples (top_k [B] int32, top_p [B] float32, min_p [B] float32), any
+    member of which may be None (that filter off).
     """
     target = np.asarray(target)
     R, V = target.shape
@@ -379,7 +423,8 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
         tl = decode_logits(target[lo:hi], dtype)
         dl = decode_logits(np.asarray(draft)[lo:hi], dtype)
         rr = verify_request(tl, dl, dt[lo:hi], float(temperature[b]), float(tau[b]), seed, b, rule,
-                            None if ts is None else ts[lo:hi], 0.0 if mc is None else float(mc[b]))
+                            None if ts is None else ts[lo:hi], 0.0 if mc is None else float(mc[b]),
+                            request_filter(target_filter, b), request_filter(draft_filter, b))
         flags[b] = rr.flags
         for rec in rr.rows:
             r = lo + rec.j

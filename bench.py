@@ -249,6 +249,99 @@ def bench_lazy(args, binding, torch, sets, ws, stream):
     print(json.dumps(line), flush=True)
 
 
+def filtered_rows(w, filt) -> int:
+    """Rows the thresholds kernel reads on one side: every row of a request with T > 0 and an
+    active filter on that side."""
+    k, tp, mp = filt
+    ro = w.row_offsets.astype(np.int64)
+    act = (w.temperature > 0) & (((k > 0) & (k < w.V)) | (tp < 1.0) | (mp > 0.0))
+    return int(np.sum(np.diff(ro)[act]))
+
+
+def bench_filtered(args, binding, torch, sets, ws, stream):
+    """K filtered verify calls (top-k / top-p / min-p on both sides), and K calls of the
+    thresholds kernel alone. The thresholds kernel's algorithmic bytes are one read of every
+    row it filters; the whole call adds pass 1's and pass 2's bytes."""
+    from lossless_rejection_sampling_row_amd import workloads as wl
+    K, W = args.steps, args.warmup
+    nsets = len(sets)
+    w0 = sets[0][0]
+    B, R, V = w0.B, w0.R, w0.V
+    esize = 2 if w0.dtype == "bf16" else 4
+    filts = []
+    for i in range(nsets):
+        tf, df = wl.sampler_filters(B, rng_seed=4242 + i)
+        dev = stream.device
+        to_t = lambda f: tuple(torch.from_numpy(a).to(dev) for a in f)  # noqa: E731
+        filts.append(((tf, df), (to_t(tf), to_t(df))))
+    out_tok = torch.empty((K, R), dtype=torch.int32, device=stream.device)
+    out_len = torch.empty((K, B), dtype=torch.int32, device=stream.device)
+    theta = torch.empty((R, 2), dtype=torch.float32, device=stream.device)
+
+    def call(i, tok, ln):
+        _, g = sets[i % nsets]
+        _, (tf, df) = filts[i % nsets]
+        binding.verify_batch(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"], g["temperature"],
+                             g["tau"], 1_000_003 * i + 17, out_tokens=tok, out_accept_len=ln, workspace=ws,
+                             stream=stream, target_filter=tf, draft_filter=df)
+
+    def thresholds(i):
+        _, g = sets[i % nsets]
+        _, (tf, df) = filts[i % nsets]
+        binding.filter_thresholds(g["target"], g["draft"], g["row_offsets"], g["temperature"], target_filter=tf,
+                                  draft_filter=df, out_theta=theta, workspace=ws, stream=stream)
+
+    def timed(fn):
+        for i in range(W):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(K):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / K
+
+    ms = timed(lambda i: call(i, out_tok[i], out_len[i]))
+    ms_th = timed(thresholds)
+    lens = out_len.cpu().numpy()
+    th_bytes = np.array([(filtered_rows(sets[i % nsets][0], filts[i % nsets][0][0])
+                          + filtered_rows(sets[i % nsets][0], filts[i % nsets][0][1])) * V * esize
+                         for i in range(K)], dtype=np.float64)
+    pair = np.array([proposal_rows(sets[i % nsets][0]) * V * 2 * esize + pass2_bytes(sets[i % nsets][0], lens[i], esize)
+                     for i in range(K)], dtype=np.float64)
+    th_gbps = th_bytes.mean() / (ms_th / 1e3) / 1e9
+    gbps = (th_bytes.mean() + pair.mean()) / (ms / 1e3) / 1e9
+    log(f"[bench] filtered verify: {ms * 1e3:.1f} us/step ({gbps:.0f} GB/s of algorithmic bytes); thresholds kernel "
+        f"alone {ms_th * 1e3:.1f} us ({th_gbps:.0f} GB/s, one read of each filtered row)")
+    line = {
+        "metric": "verified rows/sec, filtered verify (top-k / top-p / min-p on p and q)",
+        "value": round(R / (ms / 1e3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.CONFIG_NAMES[args.config] + ", sampler filters on both sides", "B": B, "rows": R,
+                   "V": V, "logits": w0.dtype, "input_sets": nsets,
+                   "filters": "per request: top_k {0,20,50}, top_p {1,0.9,0.95}, min_p {0,0.05}, each side"},
+        "thresholds_us": round(ms_th * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(th_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(th_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "thresholds_kernel",
+                     "launch_us": round(ms_th * 1e3, 2), "alg_bytes_per_launch": int(th_bytes.mean())},
+        "whole_call": {"achieved": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                       "alg_bytes_per_call": int(th_bytes.mean() + pair.mean())},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_row_sums(args, binding, torch, sets, ws, stream):
     """K calls of sv_row_acceptance over the rotating input sets. The two-pass method reads every
     proposal row twice (statistics, then the sums), so its algorithmic bytes are twice pass 1's."""
@@ -318,6 +411,8 @@ def main():
     ap.add_argument("--row-sums", action="store_true",
                     help="time the per-row acceptance sums (sv_row_acceptance) on the same inputs instead of the "
                          "verify call, and print their own JSON line")
+    ap.add_argument("--filtered", action="store_true",
+                    help="time the filtered verify (sampler filters on both sides) and its thresholds kernel")
     ap.add_argument("--lazy", action="store_true",
                     help="time the lazy position-serial verify (sv_verify_batch_lazy) instead, and print its own "
                          "JSON line; its algorithmic bytes count only the rows it must read")
@@ -374,6 +469,9 @@ def main():
         return
     if args.lazy:
         bench_lazy(args, binding, torch, sets, ws, stream)
+        return
+    if args.filtered:
+        bench_filtered(args, binding, torch, sets, ws, stream)
         return
     ev = binding.HipEvents(3 * K)
 

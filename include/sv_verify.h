@@ -108,6 +108,30 @@ typedef struct sv_batch_stats {
 } sv_batch_stats;
 
 /*
+ * The sampler's filter chain for one side (target or draft) of a batch
+ * (mlxcel PR #992, section What changed: temperature scale, then top-k, then
+ * top-p, then min-p, then the softmax of what is left). Each member is a
+ * device array of B values, one per request, or NULL, which turns that filter
+ * off for every request:
+ *   top_k  int32. Keeps the tokens whose logit is at least the k-th largest
+ *          (ties kept). 0 or >= V turns it off; a negative value is invalid.
+ *   top_p  float. On the distribution top-k leaves, renormalised: keeps the
+ *          fewest largest tokens whose mass reaches top_p, the crossing token
+ *          and its ties included. >= 1 turns it off; NaN or <= 0 is invalid.
+ *   min_p  float. Keeps the tokens whose probability is at least min_p times
+ *          the largest, tested as (x - max) / T >= ln(min_p) in fp64.
+ *          0 turns it off; NaN, < 0 or > 1 is invalid.
+ * The kept set is the tokens at or above the largest of the three
+ * thresholds, and p (or q) is the softmax over it. Filters apply only to
+ * requests with T > 0; greedy requests ignore them and their values.
+ */
+typedef struct sv_filter {
+  const int32_t* top_k;
+  const float* top_p;
+  const float* min_p;
+} sv_filter;
+
+/*
  * sv_verify_batch - verify every request of a batch.
  *
  * target_logits  [R, V] row-major, dtype. Rows that the method may read:
@@ -267,6 +291,53 @@ sv_status sv_row_acceptance(const void* target_logits, const void* draft_logits,
                             const float* temperature, const float* tau, const float* tau_step,
                             const float* min_cum, float* out_sum_min, float* out_sum_pq,
                             sv_shape shape, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * sv_filter_thresholds - each row's keep-threshold under the filter chain.
+ *
+ * For every row r of request b (T_b > 0) and each side, out_theta[2r] (target)
+ * and out_theta[2r + 1] (draft) hold a float theta such that the kept tokens
+ * are exactly those with logit >= theta: sv_filter's definition, computed
+ * exactly (top-p's masses in fp64). Rows with no active filter, and greedy
+ * requests, get -inf. A row whose logits contain NaN or +inf or are all -inf
+ * gets +inf. Values of an invalid filter are treated as off here; the verify
+ * call fails such a request.
+ * target_filter, draft_filter   host pointers to sv_filter, or NULL (no filter).
+ * out_theta      [R, 2] float (device), written in full.
+ * It reads every row of each side that has a filter at least once. Every
+ * other argument, the workspace and the errors are as for sv_verify_batch.
+ */
+sv_status sv_filter_thresholds(const void* target_logits, const void* draft_logits,
+                               const int32_t* row_offsets, const float* temperature,
+                               const sv_filter* target_filter, const sv_filter* draft_filter,
+                               float* out_theta, sv_shape shape, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
+/*
+ * sv_verify_batch_filtered - sv_verify_batch_sched with p and q filtered.
+ *
+ * p (target) and q (draft) are the filtered distributions of sv_filter, each
+ * side with its own parameters, for every row the method evaluates: the
+ * accept test, the gate mu = q * [q >= tau_j], the residual (p - mu)+ and the
+ * bonus race over p. A request with T > 0 and an invalid filter value fails
+ * closed (accept_len -1, slots -1). A filtered target's support is never left:
+ * an accepted draft has p(D) > 0, and both draws put no mass outside p's
+ * support.
+ * target_filter, draft_filter   host pointers to sv_filter, or NULL.
+ * The call first computes every row's thresholds (sv_filter_thresholds, into
+ * the workspace), then runs the two passes of sv_verify_batch with the masks.
+ * Every other argument, the results and the errors are those of
+ * sv_verify_batch_sched. With both filters NULL it computes exactly what
+ * sv_verify_batch_sched computes.
+ */
+sv_status sv_verify_batch_filtered(const void* target_logits, const void* draft_logits,
+                                   const int32_t* draft_tokens, const int32_t* row_offsets,
+                                   const float* temperature, const float* tau, const float* tau_step,
+                                   const float* min_cum, const sv_filter* target_filter,
+                                   const sv_filter* draft_filter, uint64_t seed, int32_t* out_tokens,
+                                   int32_t* out_accept_len, sv_shape shape, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream, sv_row_diag* out_row_diag,
+                                   sv_batch_stats* out_stats);
 
 /* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
 size_t sv_workspace_bytes(sv_shape shape);

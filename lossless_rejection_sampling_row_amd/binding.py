@@ -30,6 +30,11 @@ class SvShape(ctypes.Structure):
     _fields_ = [("B", c_int32), ("R", c_int32), ("V", c_int32), ("dtype", c_int32)]
 
 
+class SvFilter(ctypes.Structure):
+    """sv_filter: one side's top_k / top_p / min_p device arrays (NULL = off)."""
+    _fields_ = [("top_k", c_void_p), ("top_p", c_void_p), ("min_p", c_void_p)]
+
+
 def library_path() -> str:
     return os.environ.get("SV_LIBRARY", os.path.join(_PKG, "libsv_verify.so"))
 
@@ -57,6 +62,11 @@ def load_library():
     lib.sv_row_acceptance.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
     lib.sv_row_acceptance.restype = c_int
+    lib.sv_verify_batch_filtered.argtypes = sched[:8] + [POINTER(SvFilter), POINTER(SvFilter)] + sched[8:]
+    lib.sv_verify_batch_filtered.restype = c_int
+    lib.sv_filter_thresholds.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(SvFilter),
+                                         POINTER(SvFilter), c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
+    lib.sv_filter_thresholds.restype = c_int
     lib.sv_verify_batch_lazy.argtypes = common + [c_int]
     lib.sv_verify_batch_lazy.restype = c_int
     lib.sv_workspace_bytes.argtypes = [SvShape]
@@ -112,9 +122,23 @@ def _ptr(t):
     return c_void_p(t.data_ptr())
 
 
+def _filter_struct(filt, B: int, dev):
+    """An SvFilter from (top_k [B] int32 | None, top_p [B] float32 | None, min_p [B] float32 | None)."""
+    import torch
+    if filt is None:
+        return None
+    k, tp, mp = filt
+    for name, t, dt in (("top_k", k, torch.int32), ("top_p", tp, torch.float32), ("min_p", mp, torch.float32)):
+        if t is not None and (t.dtype != dt or t.numel() != B or t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{name}: expected contiguous {dt} [{B}] on {dev}")
+    f = SvFilter(*[None if t is None else t.data_ptr() for t in (k, tp, mp)])
+    return ctypes.byref(f), f
+
+
 def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int, *,
                  out_tokens=None, out_accept_len=None, workspace=None, row_diag=None, stats=None,
-                 events=None, stream=None, tau_step=None, min_cum=None, lazy_max_rows=None):
+                 events=None, stream=None, tau_step=None, min_cum=None, lazy_max_rows=None,
+                 target_filter=None, draft_filter=None):
     """Verify a batch of speculative windows on the GPU.
 
     target, draft : [R, V] bfloat16 or float32 (same dtype), row-major, on one GPU.
@@ -129,6 +153,9 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     tau_step      : optional [R] float32 per-row gate thresholds (see expand_schedule).
     min_cum       : optional [B] float32 cumulative floors (0 = off).
     With tau_step or min_cum the call goes to sv_verify_batch_sched (no events).
+    target_filter, draft_filter : optional (top_k, top_p, min_p) triples of [B] tensors
+                    (int32, float32, float32; any may be None). With either, the call goes to
+                    sv_verify_batch_filtered (no events).
     lazy_max_rows : with a bound on every request's rows, the call goes to sv_verify_batch_lazy,
                     which reads rows only up to each request's first rejection (plain outputs only).
     stream        : optional torch stream (default: the current stream).
@@ -177,7 +204,17 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
         raise ValueError("row_diag must be an int32 tensor with 8*R elements")
     if stats is not None and (stats.dtype != torch.int64 or stats.numel() != 8):
         raise ValueError("stats must be an int64 tensor with 8 elements")
-    if lazy_max_rows is not None:
+    if target_filter is not None or draft_filter is not None:
+        if events is not None or lazy_max_rows is not None:
+            raise ValueError("the filtered verify takes no events and has no lazy form")
+        tf = _filter_struct(target_filter, B, dev)
+        df = _filter_struct(draft_filter, B, dev)
+        fargs = args[:6] + [_ptr(tau_step) if tau_step is not None else None,
+                            _ptr(min_cum) if min_cum is not None else None,
+                            tf[0] if tf else None, df[0] if df else None] + args[6:]
+        _check(lib.sv_verify_batch_filtered(*fargs, _ptr(row_diag) if row_diag is not None else None,
+                                            _ptr(stats) if stats is not None else None))
+    elif lazy_max_rows is not None:
         if any(x is not None for x in (row_diag, stats, events, tau_step, min_cum)):
             raise ValueError("the lazy verify has plain outputs only")
         _check(lib.sv_verify_batch_lazy(*args, c_int(int(lazy_max_rows))))
@@ -197,6 +234,43 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
         _check(lib.sv_verify_batch_diag(*args, _ptr(row_diag) if row_diag is not None else None,
                                         _ptr(stats) if stats is not None else None, ev))
     return out_tokens, out_accept_len
+
+
+def filter_thresholds(target, draft, row_offsets, temperature, *, target_filter=None, draft_filter=None,
+                      out_theta=None, workspace=None, stream=None):
+    """Each row's keep-thresholds under the filter chain (sv_filter_thresholds).
+
+    Filters as for verify_batch. Returns out_theta [R, 2] float32: column 0 the target's,
+    column 1 the draft's; token x is kept iff its logit >= theta. Enqueued, not synchronised.
+    """
+    import torch
+    lib = load_library()
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU")
+    if draft.dtype != target.dtype or draft.shape != target.shape or target.dim() != 2:
+        raise ValueError("target and draft must be [R, V] tensors of one dtype")
+    if not (target.is_contiguous() and draft.is_contiguous()):
+        raise ValueError("logits must be contiguous")
+    R, V = int(target.shape[0]), int(target.shape[1])
+    B = int(row_offsets.numel()) - 1
+    for name, t, dt, n in (("row_offsets", row_offsets, torch.int32, B + 1),
+                           ("temperature", temperature, torch.float32, B)):
+        if t.dtype != dt or t.numel() != n or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {dt} [{n}] on {dev}")
+    shape = SvShape(B, R, V, dtype_code(target.dtype))
+    if out_theta is None:
+        out_theta = torch.empty((R, 2), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    tf = _filter_struct(target_filter, B, dev)
+    df = _filter_struct(draft_filter, B, dev)
+    _check(lib.sv_filter_thresholds(_ptr(target), _ptr(draft), _ptr(row_offsets), _ptr(temperature),
+                                    tf[0] if tf else None, df[0] if df else None, _ptr(out_theta), shape,
+                                    _ptr(workspace), c_size_t(workspace.numel()), c_void_p(stream.cuda_stream)))
+    return out_theta
 
 
 def row_acceptance(target, draft, draft_tokens, row_offsets, temperature, tau, *, tau_step=None, min_cum=None,

@@ -47,6 +47,8 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   off += (size_t)q.R * q.w1max * sizeof(SumPart);
   q.off_lazy = off = align_up(off, 256);  // the lazy verify's per-request stop flags
   off += (size_t)q.B * sizeof(int32_t);
+  q.off_theta = off = align_up(off, 256);  // the filtered verify's keep-thresholds: [R] (target, draft)
+  off += (size_t)q.R * 2 * sizeof(float);
   // Counters that every call leaves at zero: pass 2's request tickets, then the acceptance
   // sums' per-row done flags.
   q.off_ticket2 = off = align_up(off, 256);

@@ -46,6 +46,18 @@
 
 namespace sv {
 
+// One side's filter parameters: [B] device arrays, each optional (null: that filter off).
+struct FilterSide {
+  const int32_t* top_k;
+  const float* top_p;
+  const float* min_p;
+};
+
+struct FilterArgs {
+  FilterSide side[2];  // target, draft
+  float* theta;        // [R][2] keep-thresholds, written by thresholds_kernel
+};
+
 struct Inputs {
   const void* target;
   const void* draft;
@@ -59,7 +71,29 @@ struct Inputs {
   int32_t B, R, V, dtype;
   int32_t w1;  // pass 1: waves per row
   int32_t w2;  // pass 2: waves per request
+  // Filtered verify only: each row's keep-thresholds [R][2] (target, draft) and the filter
+  // parameters, whose validity pass 2 checks per request.
+  const float* theta = nullptr;
+  FilterSide filt[2] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
 };
+
+struct FilterParams {
+  int k;
+  float top_p, min_p;
+};
+
+__device__ __forceinline__ FilterParams filter_params(const FilterSide& f, int b) {
+  FilterParams p;
+  p.k = f.top_k != nullptr ? f.top_k[b] : 0;
+  p.top_p = f.top_p != nullptr ? f.top_p[b] : 1.0f;
+  p.min_p = f.min_p != nullptr ? f.min_p[b] : 0.0f;
+  return p;
+}
+
+// Parameter ranges. NaN fails every comparison, so a NaN top_p or min_p is invalid.
+__device__ __forceinline__ bool filter_valid(const FilterParams& p) {
+  return p.k >= 0 && p.top_p > 0.0f && p.min_p >= 0.0f && p.min_p <= 1.0f;
+}
 
 struct Work {
   WsHeader* hdr;
@@ -186,8 +220,10 @@ __device__ __forceinline__ Acc acc_empty() { return Acc{-INFINITY, 0.0f, 0.0f, I
 // Chunk u of this lane sits at vector index vb + u*64. With ARG, `am` tracks the vector
 // index of the first chunk that holds the lane's maximum: a cheap, branch-free hint of
 // where the row's large logits are (it only steers pruning in pass 2).
-template <bool ARG, class CH, int U>
-__device__ __forceinline__ void fold_soft(Acc& a, const CH (&x)[U], int vb, float c) {
+// With FILT, tokens below the row's keep-threshold th add nothing to the sum; the maximum
+// is taken over every token (the largest logit always survives the filters).
+template <bool ARG, bool FILT = false, class CH, int U>
+__device__ __forceinline__ void fold_soft(Acc& a, const CH (&x)[U], int vb, float c, float th = -INFINITY) {
   constexpr int VEC = CH::kVec;
   float vm[U];
 #pragma unroll
@@ -216,7 +252,8 @@ __device__ __forceinline__ void fold_soft(Acc& a, const CH (&x)[U], int vb, floa
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const float t = fast_exp2(fmaf(x[u].get(e), c, -a.mc));
+      float t = fast_exp2(fmaf(x[u].get(e), c, -a.mc));
+      if (FILT) t = x[u].get(e) < th ? 0.0f : t;
       if ((u * VEC + e) & 1) s1 += t; else s0 += t;
     }
   }
@@ -341,10 +378,11 @@ __device__ void block0_duties(const Inputs& in, const Work& w, const Outputs& ou
 // Stream span sp of proposal row r, both arrays, and write the wave's partial at slot g of
 // the row. ta / da already hold the span's first batch (requested by the caller, so that it
 // travels with the caller's own round trips).
-template <typename E, int VEC, int U>
+template <typename E, int VEC, int U, bool FILT = false>
 __device__ __forceinline__ void stream_span(const Inputs& in, const Work& w, int r, int g, float T, int D,
                                             const E* trow, const E* drow, Span sp, Chunk<E, VEC> (&ta)[U],
-                                            Chunk<E, VEC> (&da)[U], int lane) {
+                                            Chunk<E, VEC> (&da)[U], int lane, float th_t = -INFINITY,
+                                            float th_d = -INFINITY) {
   using CH = Chunk<E, VEC>;
   constexpr int step = U * kWave;
   CH tb[U], db[U];
@@ -360,8 +398,8 @@ __device__ __forceinline__ void stream_span(const Inputs& in, const Work& w, int
 
   auto fold_both = [&](const CH (&xt)[U], const CH (&xd)[U], int wb) __attribute__((always_inline)) {
     const int vb = wb + lane;
-    fold_soft<true>(at, xt, vb, c);
-    fold_soft<true>(ad, xd, vb, c);
+    fold_soft<true, FILT>(at, xt, vb, c, th_t);
+    fold_soft<true, FILT>(ad, xd, vb, c, th_d);
     if (holds_D) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -409,7 +447,7 @@ __device__ __forceinline__ void stream_span(const Inputs& in, const Work& w, int
   if (lane == 0) w.part1[(int64_t)r * in.w1 + g] = pp;  // read by pass 2, after this kernel
 }
 
-template <typename E, int VEC, int U>
+template <typename E, int VEC, int U, bool FILT = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void pass1_kernel(Inputs in, Work w,
                                                                                              Outputs out) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -438,6 +476,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const RowCls cls = classify_slot(in, p, bg, lane);
   if (!cls.proposal) return;
   const int r = cls.r;
+  float th_t = -INFINITY, th_d = -INFINITY;
+  if (FILT) {
+    th_t = in.theta[2 * (int64_t)r];
+    th_d = in.theta[2 * (int64_t)r + 1];
+  }
   if (r != rg) {  // the guess missed: stream the right row
     trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
     drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
@@ -447,7 +490,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
   }
 
-  stream_span<E, VEC, U>(in, w, r, g, cls.T, cls.D, trow, drow, sp, ta, da, lane);
+  stream_span<E, VEC, U, FILT>(in, w, r, g, cls.T, cls.D, trow, drow, sp, ta, da, lane, th_t, th_d);
 }
 
 // ====================================================================== pass 2
@@ -478,10 +521,11 @@ struct RowEval {
 // reach the floor). `carry` is that product over the rows before this slot set, and
 // `nlive` the number of live rows in the set; `carry` returns multiplied by the set's rows.
 // Without SCHED the threshold is ts on every row (no floor), as in the plain call.
-template <bool SCHED>
+// With FILT, p(D) and q(D) are 0 when D's logit is below the row's keep-threshold.
+template <bool SCHED, bool FILT = false>
 __device__ __forceinline__ RowEval eval_rows(const Inputs& in, const P1Part& e, bool live, int nw, int b, int j,
                                              int D, float T, float ts, float floor, double& carry, int nlive,
-                                             float c, RowStat& rs) {
+                                             float c, RowStat& rs, float th_t = -INFINITY, float th_d = -INFINITY) {
   const bool greedy = T == 0.0f;
   const float mt = seg_max(live ? e.m_t : -INFINITY, nw);
   const float md = seg_max(live ? e.m_d : -INFINITY, nw);
@@ -517,6 +561,8 @@ __device__ __forceinline__ RowEval eval_rows(const Inputs& in, const P1Part& e, 
   } else {
     p = exp2((double)ltD * (double)c - (double)mct) / st;
     q = exp2((double)ldD * (double)c - (double)mcd) / sd;
+    if (FILT && ltD < th_t) p = 0.0;
+    if (FILT && ldD < th_d) q = 0.0;
   }
   // Row group g of the set sits in lanes g*nw .. g*nw + nw - 1; every lane of a group holds
   // its row's q. The product runs over the live rows before this lane's row, in row order.
@@ -579,9 +625,11 @@ __device__ __forceinline__ P1Part pick_part(bool second, const P1Part& a, const 
 struct ReqHead {
   int lo, n;
   float T, tau;
-  float floor;  // cumulative floor (0: no cumulative gate)
+  float floor;   // cumulative floor (0: no cumulative gate)
+  bool filt_ok;  // both sides' filter values are valid (or unused: greedy)
 };
 
+template <bool FILT = false>
 __device__ __forceinline__ ReqHead request_head(const Inputs& in, int b) {
   ReqHead h;
   h.lo = in.ro[b];
@@ -589,6 +637,11 @@ __device__ __forceinline__ ReqHead request_head(const Inputs& in, int b) {
   h.T = in.temp[b];
   h.tau = in.tau[b];
   h.floor = in.min_cum != nullptr ? in.min_cum[b] : 0.0f;
+  h.filt_ok = true;
+  if (FILT) {
+    const FilterParams ft = filter_params(in.filt[0], b), fd = filter_params(in.filt[1], b);
+    h.filt_ok = h.T == 0.0f || (filter_valid(ft) && filter_valid(fd));
+  }
   return h;
 }
 
@@ -601,6 +654,7 @@ struct ReqState {
   int final_verdict;  // verdict of row f (SV_ROW_BONUS when every proposal row was accepted)
   float T, tau, c;    // after the walk, tau is row f's gate threshold
   float floor;        // cumulative floor
+  float th_t, th_d;   // row f's keep-thresholds (-inf without filters)
   RowStat stop;       // row f's statistics when f is a proposal row
   int stop_half;      // row f's partials are in e1 (1) or e0 (0) ...
   int stop_lane0;     // ... in lanes stop_lane0 .. stop_lane0 + w1 - 1
@@ -621,6 +675,13 @@ __device__ __forceinline__ void prefetch_rows(const Inputs& in, const Work& w, i
   e1 = w.part1[min(base + lane + kWave, last)];
 }
 
+// Keep-thresholds of rows lo .. lo+63 (lane j: row lo + j), clamped into the array.
+__device__ __forceinline__ void prefetch_theta(const Inputs& in, int lo, int lane, float& tht0, float& thd0) {
+  const int64_t r = min(lo + lane, in.R - 1);
+  tht0 = in.theta[2 * r];
+  thd0 = in.theta[2 * r + 1];
+}
+
 // Rebuild request b (head h, row_offsets checked) from the inputs and pass 1's partials:
 // test its proposal rows in order up to the first one that is not accepted. Every wave of
 // the request does this on its own, so no wave waits for another. dt0/e0/e1 arrive
@@ -628,10 +689,11 @@ __device__ __forceinline__ void prefetch_rows(const Inputs& in, const Work& w, i
 // one slot are tested together. On return e0/e1 hold the slot set with row f. With
 // `diag`, each row's record is written once: tested rows by their group's first lane (the
 // stop row with `stop_resid`), untested and bonus rows after the walk.
-template <bool SCHED>
+template <bool SCHED, bool FILT = false>
 __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w, int b, const ReqHead& h,
                                                  int lo_pre, int lane, int dt0, float ts0, P1Part& e0, P1Part& e1,
-                                                 sv_row_diag* diag, float stop_resid) {
+                                                 sv_row_diag* diag, float stop_resid, float tht0 = -INFINITY,
+                                                 float thd0 = -INFINITY) {
   ReqState q{};
   q.lo = h.lo;
   q.n = h.n;
@@ -640,14 +702,18 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   q.floor = SCHED ? h.floor : 0.0f;
   q.stop_half = 0;
   q.stop_lane0 = 0;
+  q.th_t = q.th_d = -INFINITY;
   const bool req_ok = temperature_ok(q.T) && !__builtin_isnan(q.tau) && __builtin_isfinite(q.floor) &&
-                      q.floor >= 0.0f;
+                      q.floor >= 0.0f && h.filt_ok;
   q.c = req_ok ? fold_scale(q.T) : 0.0f;
   const int nw = in.w1;
   const int rows_half = kWave / nw;
   const int per_group = 2 * rows_half;
   const int nd = q.n - 1;  // rows that carry a drafted token: all but the last
-  if (q.lo != lo_pre) prefetch_rows<SCHED>(in, w, q.lo, lane, dt0, ts0, e0, e1);  // requests of different lengths
+  if (q.lo != lo_pre) {  // requests of different lengths
+    prefetch_rows<SCHED>(in, w, q.lo, lane, dt0, ts0, e0, e1);
+    if (FILT) prefetch_theta(in, q.lo, lane, tht0, thd0);
+  }
   // Proposal rows: the rows before the first drafted token outside [0, V).
   q.n_prop = nd;
   for (int base = 0; base < nd; base += kWave) {
@@ -686,9 +752,14 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
       const float ts = !SCHED || in.tau_step == nullptr ? q.tau
                                                         : jc < kWave ? __shfl(ts0, jc) : in.tau_step[q.lo + jc];
       const int nlive = min(rows_half, q.n_prop - jh);
+      float th_t = -INFINITY, th_d = -INFINITY;
+      if (FILT) {
+        th_t = jc < kWave ? __shfl(tht0, jc) : in.theta[2 * (int64_t)(q.lo + jc)];
+        th_d = jc < kWave ? __shfl(thd0, jc) : in.theta[2 * (int64_t)(q.lo + jc) + 1];
+      }
       RowStat rs;
-      const RowEval ev = eval_rows<SCHED>(in, pick_part(half != 0, e0, e1), live, nw, b, j, D, q.T, ts, q.floor, carry,
-                                   nlive, q.c, rs);
+      const RowEval ev = eval_rows<SCHED, FILT>(in, pick_part(half != 0, e0, e1), live, nw, b, j, D, q.T, ts,
+                                                q.floor, carry, nlive, q.c, rs, th_t, th_d);
       const uint64_t m = __ballot(live && ev.verdict != SV_ROW_ACCEPT);
       int stop_j = INT32_MAX;
       if (m != 0) {
@@ -720,6 +791,10 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   q.k = k;
   q.f = q.lo + k;
   q.tau = stop_tau;
+  if (FILT) {
+    q.th_t = k < kWave ? __shfl(tht0, k) : in.theta[2 * (int64_t)q.f];
+    q.th_d = k < kWave ? __shfl(thd0, k) : in.theta[2 * (int64_t)q.f + 1];
+  }
   const bool greedy = q.T == 0.0f;
   if (k < q.n_prop) {
     q.kind = q.final_verdict == kRowInvalid ? kKindInvalid : greedy ? kKindGreedyDone : kKindResidual;
@@ -745,6 +820,8 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   q.kind = uni(q.kind);
   q.final_verdict = uni(q.final_verdict);
   q.tau = uni(q.tau);
+  q.th_t = uni(q.th_t);
+  q.th_d = uni(q.th_d);
   q.stop.m_t = uni(q.stop.m_t);
   q.stop.mc_t = uni(q.stop.mc_t);
   q.stop.m_d = uni(q.stop.m_d);
@@ -777,6 +854,7 @@ __device__ __forceinline__ void add_stats(const Outputs& out, const ReqState& q,
 
 // Write request b's outputs (one wave): the accepted drafts, the last token, -1 after it.
 // A request that fails closed gets -1 everywhere and untested diagnostics.
+template <bool FILT = false>
 __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, const Outputs& out, int b,
                                              const ReqState& q, bool invalid, int token, float resid, int lane) {
   for (int j = lane; j < q.n; j += kWave) {
@@ -794,8 +872,11 @@ __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, co
       int dt0;
       float ts0;
       P1Part e0, e1;
+      float tht0 = -INFINITY, thd0 = -INFINITY;
       prefetch_rows<true>(in, w, q.lo, lane, dt0, ts0, e0, e1);
-      walk_request<true>(in, w, b, request_head(in, b), q.lo, lane, dt0, ts0, e0, e1, out.diag, resid);
+      if (FILT) prefetch_theta(in, q.lo, lane, tht0, thd0);
+      walk_request<true, FILT>(in, w, b, request_head<FILT>(in, b), q.lo, lane, dt0, ts0, e0, e1, out.diag, resid,
+                               tht0, thd0);
     }
   }
 }
@@ -808,10 +889,12 @@ constexpr float kKeyErr = 1e-5f;
 constexpr float kLogKeySlack = 0.01f;
 
 // fp64 race key of token x on a residual row, from its two logits.
+// Logits below a keep-threshold (th_t, th_d) give p = 0 or q = 0.
 __device__ __forceinline__ double residual_key64(double lt, double ld, double c, double mct, double mcd,
-                                                 double st, double sd, double tau, uint32_t word) {
-  const double p = exp2(lt * c - mct) / st;
-  const double q = exp2(ld * c - mcd) / sd;
+                                                 double st, double sd, double tau, uint32_t word,
+                                                 float th_t, float th_d) {
+  const double p = (float)lt < th_t ? 0.0 : exp2(lt * c - mct) / st;
+  const double q = (float)ld < th_d ? 0.0 : exp2(ld * c - mcd) / sd;
   const double mu = q >= tau ? q : 0.0;
   const double r = p - mu;
   if (!(r > 0.0)) return 0.0;
@@ -852,7 +935,7 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
   for (int64_t x = lane; x < in.V; x += kWave) {
     const float l = logit_at(in.target, in.dtype, (int64_t)q.f * in.V + x);
     const float a = l * q.c;
-    if (a > -INFINITY) {
+    if (a > -INFINITY && !(l < q.th_t)) {
       const uint32_t wd = race_word(in.seed, x, q.k, b);
       top2_push(t, a - log2_expo32(wd), (int)x, l, 0.0f);
     }
@@ -872,7 +955,8 @@ __device__ __forceinline__ int p_race_one_wave(const Inputs& in, const ReqState&
 // The plain call's waves skip, by one test in the logit domain, every 16-byte vector that
 // cannot hold a race candidate: r = (p - mu)+ <= p, so a vector whose largest p is below the
 // pruning threshold holds none, whatever mu is.
-template <typename E, int VEC, int U, bool DIAG>
+// With FILT (the filtered verify) every p and q is masked by its row's keep-threshold.
+template <typename E, int VEC, int U, bool DIAG, bool FILT = false>
 __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Outputs out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -886,12 +970,14 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   // tokens and partials at the first row the head would give if every request had the
   // same length.
   const int ro_valid = w.hdr->ro_valid;
-  const ReqHead rh = request_head(in, b);
+  const ReqHead rh = request_head<FILT>(in, b);
   const int lo_pre = (int)((int64_t)b * in.R / in.B);
   int dt0;
   float ts0;
   P1Part e0, e1;
   prefetch_rows<DIAG>(in, w, lo_pre, lane, dt0, ts0, e0, e1);
+  float tht0 = -INFINITY, thd0 = -INFINITY;
+  if (FILT) prefetch_theta(in, lo_pre, lane, tht0, thd0);
   if (!ro_valid) {
     // Broken row_offsets: the whole batch fails closed. The head wave of request b
     // clears an even share of the rows.
@@ -909,15 +995,15 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     return;
   }
 
-  const ReqState q = walk_request<DIAG>(in, w, b, rh, lo_pre, lane, dt0, ts0, e0, e1, nullptr, NAN);
+  const ReqState q = walk_request<DIAG, FILT>(in, w, b, rh, lo_pre, lane, dt0, ts0, e0, e1, nullptr, NAN, tht0, thd0);
   if (q.kind == kKindInvalid) {
-    if (head) emit_request(in, w, out, b, q, true, -1, NAN, lane);
+    if (head) emit_request<FILT>(in, w, out, b, q, true, -1, NAN, lane);
     return;
   }
   if (q.kind == kKindGreedyDone) {
     // One-hot p and mu: the residual is empty iff the offered draft argmax is the target argmax.
     const float resid = (q.stop.am_t == q.stop.am_d && 1.0f >= q.tau) ? 0.0f : 1.0f;
-    if (head) emit_request(in, w, out, b, q, false, q.stop.am_t, resid, lane);
+    if (head) emit_request<FILT>(in, w, out, b, q, false, q.stop.am_t, resid, lane);
     return;
   }
 
@@ -939,9 +1025,12 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   part.mref = -INFINITY;
   part.bad = 0;
   part.gidx = -1;
+  part.pidx = -1;
+  part.pkey = -INFINITY;
 
   if (q.kind == kKindResidual) {
     const float c = q.c, mct = q.stop.mc_t, mcd = q.stop.mc_d, tau = q.tau;
+    const float tht = q.th_t, thd = q.th_d;
     const float ist = (float)(1.0 / q.stop.s_t), isd = (float)(1.0 / q.stop.s_d);
     // Gate in the logit domain: q_x >= tau needs l_d*c - mcd >= log2(tau * s_d). The margin
     // keeps every token whose fp32 q could reach tau; for the others mu = 0 and r = p, so q
@@ -978,8 +1067,8 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     float kh = 0.0f;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const float p = fast_exp2(fmaf(hlt[s], c, -mct)) * ist;
-      const float qq = fast_exp2(fmaf(hld[s], c, -mcd)) * isd;
+      const float p = (FILT && hlt[s] < tht) ? 0.0f : fast_exp2(fmaf(hlt[s], c, -mct)) * ist;
+      const float qq = (FILT && hld[s] < thd) ? 0.0f : fast_exp2(fmaf(hld[s], c, -mcd)) * isd;
       const float mu = qq >= tau ? qq : 0.0f;
       const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
       if (hx[s] >= 0 && rl > 0.0f)
@@ -997,6 +1086,14 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 
     float rsum = 0.0f;
     Top2 t = top2_empty();
+    // With a target filter, p often has few tokens and p <= mu on all of them, which leaves
+    // the residual empty: the draw then races over p. The waves track that race too, over
+    // the kept tokens whose l*c is within 29 of the row maximum's (a token further below
+    // cannot win a log2-key race; see the bonus race). No vector is skipped while the
+    // residual may be empty: skipping needs a drawn candidate with r > 0.
+    const bool prace = FILT && tht > -INFINITY;
+    const float plb = q.stop.m_t * c - 29.0f;
+    Top2 tq = top2_empty();
     auto fold_res = [&](const CH (&xt)[U], const CH (&xd)[U], int v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1012,6 +1109,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           rv[e] = fast_exp2(fmaf(xt[u].get(e), c, -mct)) * ist;  // p; r = p where mu = 0
+          if (FILT && xt[u].get(e) < tht) rv[e] = 0.0f;
           mv[e] = 0.0f;
           gated |= xd[u].get(e) >= gate_l;
         }
@@ -1019,12 +1117,12 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             const float qq = fast_exp2(fmaf(xd[u].get(e), c, -mcd)) * isd;
-            mv[e] = qq >= tau ? qq : 0.0f;
+            mv[e] = (qq >= tau && !(FILT && xd[u].get(e) < thd)) ? qq : 0.0f;
           }
         }
 #pragma unroll
         for (int gg = 0; gg < VEC; gg += G) {
-          bool any = false;
+          bool any = false, anyp = false;
 #pragma unroll
           for (int e = 0; e < G; ++e) {
             const float p = rv[gg + e], mu = mv[gg + e];
@@ -1032,8 +1130,9 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
             mv[gg + e] = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
             if (DIAG) rsum += rv[gg + e];
             any |= (rv[gg + e] > 0.0f && rv[gg + e] >= pthr);
+            if (prace) anyp |= !(xt[u].get(gg + e) < tht) && xt[u].get(gg + e) * c >= plb;
           }
-          if (any) {
+          if (any || anyp) {
             const int xg = x0 + gg;
             const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
 #pragma unroll
@@ -1044,6 +1143,13 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
                 const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
                 top2_push(t, div_fast(r, expo32(wd)), x, xt[u].get(gg + e), xd[u].get(gg + e));
                 safe = fmaxf(safe, div_fast(mv[gg + e], expo32_upper(wd)) * (1.0f - kKeyErr));
+              }
+              if (prace) {
+                const float l = xt[u].get(gg + e);
+                if (!(l < tht) && l * c >= plb) {
+                  const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, (xg + e) & 3);
+                  top2_push(tq, l * c - log2_expo32(wd), xg + e, l, 0.0f);
+                }
               }
             }
           }
@@ -1071,11 +1177,22 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     resolve_race(t, wave_max(t.k1) * (1.0f - kRatioKeySlack),
                  [&](int x, float lt, float ld) {
                    return residual_key64((double)lt, (double)ld, (double)c, (double)mct, (double)mcd, q.stop.s_t,
-                                         q.stop.s_d, (double)tau, race_word(in.seed, x, q.k, b));
+                                         q.stop.s_d, (double)tau, race_word(in.seed, x, q.k, b), tht, thd);
                  },
                  bk, bi);
     part.key = bk;
     part.idx = bi == INT32_MAX ? -1 : bi;
+    if (prace) {
+      double pk;
+      int pi;
+      resolve_race(tq, wave_max(tq.k1) - kLogKeySlack,
+                   [&](int x, float l, float) {
+                     return p_logkey64((double)l, (double)q.T, race_word(in.seed, x, q.k, b));
+                   },
+                   pk, pi);
+      part.pkey = pk;
+      part.pidx = pi == INT32_MAX ? -1 : pi;
+    }
   } else {
     // Bonus row (race over p) or greedy bonus row (argmax). Pass 1 never read it, so it is validated here.
     const bool race = q.kind == kKindBonus;
@@ -1105,6 +1222,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 #pragma unroll
             for (int e = 0; e < G; ++e) {
               av[e] = xt[u].get(gg + e) * c;
+              if (FILT && xt[u].get(gg + e) < q.th_t) av[e] = -INFINITY;  // outside p's support
               any |= av[e] + 25.0f >= lb;
             }
             if (any) {
@@ -1179,8 +1297,23 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     resid = DIAG ? (float)R : NAN;
     // A drawn candidate has r > 0 (also in fp32), so a positive best key means the residual
     // has mass, and no candidate means none outside decision-boundary requests.
-    if (bk > 0.0) token = bi;
-    else token = p_race_one_wave(in, q, b, lane);  // residual with no mass: race over p
+    if (bk > 0.0) {
+      token = bi;
+    } else if (FILT && q.th_t > -INFINITY) {  // residual with no mass: the waves' race over p
+      double pk = -INFINITY;
+      int pi = INT32_MAX;
+      for (int i = lane; i < nw; i += kWave) {
+        const P2Part c2 = read_record(pp + i);
+        if (c2.pidx >= 0 && beats(c2.pkey, c2.pidx, pk, pi)) {
+          pk = c2.pkey;
+          pi = c2.pidx;
+        }
+      }
+      wave_best(pk, pi);
+      token = pi != INT32_MAX ? pi : p_race_one_wave(in, q, b, lane);
+    } else {
+      token = p_race_one_wave(in, q, b, lane);  // residual with no mass: race over p
+    }
   } else {
     float M = -INFINITY;
     int bad = 0;
@@ -1211,7 +1344,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       token = bi;
     }
   }
-  emit_request(in, w, out, b, q, invalid, token, resid, lane);
+  emit_request<FILT>(in, w, out, b, q, invalid, token, resid, lane);
 }
 
 // ====================================================================== lazy verify
@@ -1406,6 +1539,384 @@ __global__ __launch_bounds__(kBlock) void merge_sums_kernel(Inputs in, Work w, f
 
 // Zero the request tickets. Every ticket wraps back to zero when a call completes, so this
 // runs only when a workspace is first seen or its layout changes (see counters_ready).
+// ====================================================================== filter chain
+
+// The sampler's filter chain (mlxcel PR #992, section What changed): temperature scale,
+// top-k, then top-p on what top-k leaves, then min-p. Each filter keeps the tokens whose
+// logit reaches a threshold, ties included, so one float per row and side describes the
+// kept set: token x is kept iff !(l_x < theta). One workgroup finds theta for one row and
+// side.
+//  - Pass A reads the row for its maximum m and validity. min-p's threshold follows from m
+//    alone: the smallest float y with (y - m) / T >= ln(min_p) in fp64.
+//  - Pass B gathers into LDS the logits that can hold the thresholds: those at or above the
+//    k-th largest of the threads' maxima (top-k), or within W = log2(V / (1 - top_p)) + 1
+//    log2 units of mass below m (top-p alone, which holds its crossing), and sums the fp32
+//    mass of the others.
+//  - The candidates are sorted (bitonic, in LDS). top-k's threshold is the k-th; top-p's is
+//    where the fp64 prefix mass of exp((l - m) / T) first reaches top_p times top-k's mass.
+//  - When the window holds more than kCandCap logits, or fewer than top-k's k, the filters
+//    are decided by bisection over the float order, one pass over the row per step: top-k
+//    on counts (after which top-k's set is gathered for top-p when it fits), top-p on fp64
+//    masses. Exact; the second is slow. Peaked rows keep the window small.
+constexpr int kCandCap = 8192;  // candidate logits one workgroup sorts in LDS
+
+// Total order on non-NaN floats as int32: order_key(a) < order_key(b) iff a < b, with -0
+// just below +0.
+__device__ __forceinline__ int32_t order_key(float f) {
+  const int32_t i = __float_as_int(f);
+  return i >= 0 ? i : i ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float key_float(int32_t k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
+
+struct FilterSmem {
+  float cand[kCandCap];
+  double red[kWavesPerBlock];
+  int n_cand, first;
+};
+
+__device__ __forceinline__ double block_sum(double v, FilterSmem& s) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s.red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) t += s.red[w];
+  return t;
+}
+
+__device__ __forceinline__ float block_max(float v, FilterSmem& s) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s.red[threadIdx.x / kWave] = (double)v;
+  __syncthreads();
+  float t = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) t = fmaxf(t, (float)s.red[w]);
+  return t;
+}
+
+// Walk a row with every thread of the workgroup: step st covers vectors
+// [st * kBlock * kFiltLoads, (st + 1) * kBlock * kFiltLoads), kFiltLoads per thread, strided
+// by kBlock. Every lane runs every step (a lane past the row's end re-reads the row's last
+// vector, a cache hit, and sees ok = false), so the step function may use wave-wide
+// operations. Loads are double-buffered: the next step's vectors are in flight while
+// step(x, ok, st) works on the current ones.
+constexpr int kFiltLoads = 4;
+
+template <typename E, int VEC, class S>
+__device__ __forceinline__ void walk_row(const E* row, int nvec, S step) {
+  using CH = Chunk<E, VEC>;
+  constexpr int per = kBlock * kFiltLoads;
+  const int steps = (nvec + per - 1) / per;
+  auto load = [&](CH (&x)[kFiltLoads], int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kFiltLoads; ++u)
+      x[u].load(row + (int64_t)min(st * per + u * kBlock + (int)threadIdx.x, nvec - 1) * VEC);
+  };
+  auto run = [&](const CH (&x)[kFiltLoads], int st) __attribute__((always_inline)) {
+    bool ok[kFiltLoads];
+#pragma unroll
+    for (int u = 0; u < kFiltLoads; ++u) ok[u] = st * per + u * kBlock + (int)threadIdx.x < nvec;
+    step(x, ok, st);
+  };
+  CH xa[kFiltLoads], xb[kFiltLoads];
+  if (steps > 0) load(xa, 0);
+  for (int st = 0; st < steps; st += 2) {  // an odd count ends with a step that is all ok = false
+    load(xb, st + 1);
+    run(xa, st);
+    load(xa, st + 2);
+    run(xb, st + 1);
+  }
+}
+
+// Run f(x) on every logit of a row (no wave-wide operations in f).
+template <typename E, int VEC, class F>
+__device__ __forceinline__ void for_each_logit(const E* row, int nvec, F f) {
+  walk_row<E, VEC>(row, nvec, [&](const Chunk<E, VEC>(&x)[kFiltLoads], const bool (&ok)[kFiltLoads], int)
+                                  __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kFiltLoads; ++u)
+      if (ok[u]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) f(x[u].get(e));
+      }
+  });
+}
+
+// Number of logits >= v.
+template <typename E, int VEC>
+__device__ __noinline__ double count_ge(const E* row, int nvec, float v, FilterSmem& s) {
+  int n = 0;
+  for_each_logit<E, VEC>(row, nvec, [&](float x) __attribute__((always_inline)) { n += !(x < v); });
+  return block_sum((double)n, s);
+}
+
+// fp64 mass of the logits >= v: sum of exp((l - m) / T).
+template <typename E, int VEC>
+__device__ __noinline__ double mass_ge(const E* row, int nvec, float v, float m, double T, FilterSmem& s) {
+  double t = 0.0;
+  for_each_logit<E, VEC>(row, nvec, [&](float x) __attribute__((always_inline)) {
+    if (!(x < v)) t += exp(((double)x - (double)m) / T);
+  });
+  return block_sum(t, s);
+}
+
+// Largest float v in [lo, hi] with pred(v), by bisection over order_key; pred(lo) holds and
+// pred is monotone (true below some point, false above).
+template <class P>
+__device__ float bisect_float(float lo, float hi, P pred) {
+  int64_t a = order_key(lo), z = order_key(hi);
+  if (pred(key_float((int32_t)z))) return hi;
+  while (z - a > 1) {
+    const int64_t mid = a + (z - a) / 2;
+    if (pred(key_float((int32_t)mid))) a = mid;
+    else z = mid;
+  }
+  return key_float((int32_t)a);
+}
+
+template <typename E, int VEC>
+__global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArgs fa) {
+  __shared__ FilterSmem s;
+  const int r = blockIdx.x;
+  const int side = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  float* out = fa.theta + 2 * (int64_t)r + side;
+
+  // The row's request: the guess for equal lengths, else a binary search. Every index stays
+  // in bounds whatever row_offsets holds (a broken batch fails in pass 2).
+  int b = min((int)(((int64_t)r * in.B) / in.R), in.B - 1);
+  if (!(in.ro[b] <= r && r < in.ro[b + 1])) {
+    int L = 0, H = in.B - 1;
+    while (L < H) {
+      const int mid = (L + H + 1) >> 1;
+      if (in.ro[mid] <= r) L = mid; else H = mid - 1;
+    }
+    b = L;
+  }
+  const float T = in.temp[b];
+  const FilterParams fp = filter_params(fa.side[side], b);
+  const bool topk = fp.k > 0 && fp.k < in.V;
+  const bool topp = fp.top_p < 1.0f;
+  const bool minp = fp.min_p > 0.0f;
+  if (!(T > 0.0f) || !temperature_ok(T) || !filter_valid(fp) || !(topk || topp || minp)) {
+    if (threadIdx.x == 0) *out = -INFINITY;
+    return;
+  }
+  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
+  const int nvec = in.V / VEC;
+  const double Td = (double)T;
+
+  // Sort s.cand[0, n) largest first (bitonic, padded with -inf).
+  auto sort_desc = [&](int n) __attribute__((always_inline)) {
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    for (int i = n + threadIdx.x; i < np2; i += kBlock) s.cand[i] = -INFINITY;
+    __syncthreads();
+    for (int k = 2; k <= np2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = threadIdx.x; i < np2; i += kBlock) {
+          const int ij = i ^ j;
+          if (ij > i) {
+            const float a = s.cand[i], z = s.cand[ij];
+            if (((i & k) == 0) ? (a < z) : (a > z)) {
+              s.cand[i] = z;
+              s.cand[ij] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  };
+  // ---- pass A: maximum and validity
+  float mx = -INFINITY;
+  int bad = 0;
+  for_each_logit<E, VEC>(row, nvec, [&](float x) __attribute__((always_inline)) {
+    mx = fmaxf(mx, x);
+    bad |= (int)(__builtin_isnan(x) || x == INFINITY);
+  });
+  const float m = block_max(mx, s);
+  const bool valid = block_sum((double)bad, s) == 0.0 && m != -INFINITY;
+  if (!valid) {
+    if (threadIdx.x == 0) *out = INFINITY;
+    return;
+  }
+  // min-p: the smallest float y with (y - m) / T >= ln(min_p), in fp64.
+  float th_m = -INFINITY;
+  if (minp) {
+    const double lm = log((double)fp.min_p);
+    auto keep = [&](float y) { return ((double)y - (double)m) / Td >= lm; };
+    float y = (float)((double)m + Td * lm);
+    for (int it = 0; it < 64 && !keep(y); ++it) y = nextafterf(y, INFINITY);
+    for (int it = 0; it < 64 && keep(nextafterf(y, -INFINITY)); ++it) y = nextafterf(y, -INFINITY);
+    th_m = y;
+  }
+  if (!topk && !topp) {
+    if (threadIdx.x == 0) *out = th_m;
+    return;
+  }
+
+  // ---- the candidates to gather
+  //  - With top-k (k <= kBlock): the logits at or above the k-th largest of the threads'
+  //    maxima. At least k logits reach it, so it is at most top-k's threshold; and top-p's
+  //    crossing lies above top-k's threshold.
+  //  - With top-p alone: the logits within W = log2(V / (1 - top_p)) + 1 log2 units of mass
+  //    below the maximum. A logit below that has mass under 2^-W of the maximum's, so all of
+  //    them together hold less than V * 2^-W < (1 - top_p) of the row's mass (which holds
+  //    the maximum): the crossing lies inside.
+  //  - With top-k beyond kBlock alone: a 24-unit window, a guess checked below.
+  const float c = scale_of(T);  // log2(e) / T
+  const float W = topp ? log2f((float)in.V / (1.0f - fp.top_p)) + 1.0f : 24.0f;
+  float edge = -INFINITY;
+  const bool by_edge = topk && fp.k <= kBlock;
+  if (by_edge) {
+    s.cand[threadIdx.x] = mx;  // -inf for a thread that read nothing
+    sort_desc(kBlock);
+    edge = s.cand[fp.k - 1];
+    __syncthreads();
+  }
+  // One bound for both: the gathered logits are those >= lo. The window's bound sits a little
+  // below m - W / c, so that fp32 rounding can only widen it.
+  const float lo = by_edge ? edge : m - (W + 0.01f) / c;
+  // ---- gather, sort, scan
+  // gather(lo, ...): the logits >= lo go to s.cand. Returns how many there are (those past
+  // kCandCap are counted, not stored).
+  // Per step each lane counts its candidates and, holding any, reserves their slots with one
+  // LDS atomic and stores them. With sum_rest, the fp32 mass of the
+  // other logits goes to `rest` (per vector in fp32, per lane in fp64).
+  auto gather = [&](const float lo, const bool sum_rest, double& rest) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) s.n_cand = 0;
+    __syncthreads();
+    double tl = 0.0;
+    walk_row<E, VEC>(row, nvec, [&](const Chunk<E, VEC>(&x)[kFiltLoads], const bool (&ok)[kFiltLoads], int)
+                                    __attribute__((always_inline)) {
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < kFiltLoads; ++u) {
+        float ts = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float v = x[u].get(e);
+          const bool cand = ok[u] && !(v < lo);
+          cnt += cand ? 1 : 0;
+          if (sum_rest && ok[u] && !cand) ts += fast_exp2((v - m) * c);
+        }
+        if (sum_rest) tl += (double)ts;
+      }
+      if (cnt == 0) return;
+      int slot = atomicAdd(&s.n_cand, cnt);  // candidates are sparse: one LDS atomic per lane holding any
+#pragma unroll
+      for (int u = 0; u < kFiltLoads; ++u) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float v = x[u].get(e);
+          if (ok[u] && !(v < lo)) {
+            if (slot < kCandCap) s.cand[slot] = v;
+            ++slot;
+          }
+        }
+      }
+    });
+    rest = block_sum(tl, s);  // its barriers also publish s.n_cand and s.cand
+    return s.n_cand;
+  };
+  // top-p over the sorted candidates s.cand[0, nk), which hold top-k's whole set; S1 is their
+  // fp64 mass plus `extra` (the mass of top-k's set outside them). Returns the logit at the
+  // first position whose prefix mass reaches top_p * S1, or NaN when the candidates hold less.
+  auto top_p_scan = [&](int nk, double extra) __attribute__((always_inline)) {
+    const int ch = (nk + kBlock - 1) / kBlock;
+    const int i0 = min((int)threadIdx.x * ch, nk), i1 = min(i0 + ch, nk);
+    double own = 0.0;
+    for (int i = i0; i < i1; ++i) own += exp(((double)s.cand[i] - (double)m) / Td);
+    double incl = own;  // inclusive prefix over the wave's lanes, then over the waves
+    for (int d = 1; d < kWave; d <<= 1) {
+      const double t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) s.red[wave] = incl;
+    if (threadIdx.x == 0) s.first = INT32_MAX;
+    __syncthreads();
+    double before = 0.0, total = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      before += w < wave ? s.red[w] : 0.0;
+      total += s.red[w];
+    }
+    const double target = (double)fp.top_p * (total + extra);
+    double run = before + incl - own;  // exclusive prefix of this thread's chunk
+    for (int i = i0; i < i1; ++i) {
+      run += exp(((double)s.cand[i] - (double)m) / Td);
+      if (run >= target) {
+        atomicMin(&s.first, i);
+        break;
+      }
+    }
+    __syncthreads();
+    const int ip = s.first;
+    const float th = ip != INT32_MAX ? s.cand[ip] : NAN;
+    __syncthreads();
+    return th;
+  };
+  // Candidates at or above th in the sorted s.cand[0, n), given that the first k are.
+  auto count_prefix = [&](int n, int k, float th) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) s.first = n;
+    __syncthreads();
+    for (int i = k - 1 + threadIdx.x; i < n - 1; i += kBlock)
+      if (s.cand[i + 1] < th) atomicMin(&s.first, i + 1);
+    __syncthreads();
+    const int nk = s.first;
+    __syncthreads();
+    return nk;
+  };
+
+  float th_k = -INFINITY, th_p = -INFINITY;
+  bool have_k = !topk;  // top-k's threshold is known
+  int n = -1;           // sorted candidates in s.cand (-1: none usable)
+  double rest = 0.0;    // fp32 mass of the logits outside them
+  {
+    const int nw = gather(lo, topp && !topk, rest);
+    if (nw <= kCandCap) {
+      n = nw;
+      sort_desc(n);
+      if (topk && n >= fp.k) {
+        th_k = s.cand[fp.k - 1];
+        have_k = true;
+      }
+    }
+  }
+  if (!have_k) {
+    // More logits lie above top-k's threshold than the cut gathered: bisect on counts, then
+    // gather top-k's set for top-p when it fits.
+    const double kk = (double)fp.k;
+    th_k = bisect_float(-INFINITY, m, [&](float v) { return count_ge<E, VEC>(row, nvec, v, s) >= kk; });
+    have_k = true;
+    n = -1;
+    if (topp && count_ge<E, VEC>(row, nvec, th_k, s) <= (double)kCandCap) {
+      n = gather(th_k, false, rest);
+      sort_desc(n);
+    }
+  }
+  if (topp) {
+    float th = NAN;
+    if (n >= 0) {
+      if (topk) th = top_p_scan(count_prefix(n, min(fp.k, n), th_k), 0.0);  // S1: top-k's set, all gathered
+      else th = top_p_scan(n, rest);                                          // S1: the whole row
+    }
+    if (__builtin_isnan(th)) {
+      // The candidates hold less than top_p of the mass: bisect on fp64 masses.
+      const double S1 = mass_ge<E, VEC>(row, nvec, th_k, m, Td, s);
+      const double target = (double)fp.top_p * S1;
+      th = bisect_float(th_k, m, [&](float v) { return mass_ge<E, VEC>(row, nvec, v, m, Td, s) >= target; });
+    }
+    th_p = th;
+  }
+  if (threadIdx.x == 0) *out = fmaxf(fmaxf(th_k, th_p), th_m);
+}
+
 __global__ __launch_bounds__(kBlock) void clear_counters_kernel(uint32_t* t, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) t[i] = 0u;
@@ -1477,15 +1988,23 @@ static hipError_t resident_waves(const void* fn, int per_cu_target, int64_t* slo
   return hipSuccess;
 }
 
+// The filtered verify's first kernel: every row's keep-thresholds, one workgroup per row
+// and side.
 template <typename E, int VEC>
+hipError_t launch_thresholds(const Plan& p, const Inputs& in, const FilterArgs& fa, hipStream_t stream) {
+  hipLaunchKernelGGL((thresholds_kernel<E, VEC>), dim3((unsigned)p.R, 2u), dim3(kBlock), 0, stream, in, fa);
+  return hipGetLastError();
+}
+
+template <typename E, int VEC, bool FILT = false>
 hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& out, hipStream_t stream,
                        hipEvent_t const* ev) {
   constexpr int U1 = VEC == 1 ? 8 : 2;  // pass 1: chunks per lane per array and step (x2 buffers)
   constexpr int U2 = VEC == 1 ? 8 : 2;  // pass 2: the same
-  const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
+  const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1, FILT>);
   const bool diag = out.diag != nullptr || in.tau_step != nullptr || in.min_cum != nullptr;
-  const void* k2 = diag ? reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, true>)
-                        : reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, false>);
+  const void* k2 = diag ? reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, true, FILT>)
+                        : reinterpret_cast<const void*>(&pass2_kernel<E, VEC, U2, false, FILT>);
   int64_t slots1 = 0, slots2 = 0;
   hipError_t err = resident_waves(k1, kTargetWavesPerCU, &slots1);
   if (err != hipSuccess) return err;
@@ -1495,13 +2014,15 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   in.w2 = l.w2;
   if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
   const dim3 block(kBlock);
-  hipLaunchKernelGGL((pass1_kernel<E, VEC, U1>), dim3((unsigned)l.blocks1), block, 0, stream, in, w, out);
+  hipLaunchKernelGGL((pass1_kernel<E, VEC, U1, FILT>), dim3((unsigned)l.blocks1), block, 0, stream, in, w, out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
   if (diag)
-    hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, true>), dim3((unsigned)l.blocks2), block, 0, stream, in, w, out);
+    hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, true, FILT>), dim3((unsigned)l.blocks2), block, 0, stream, in, w,
+                       out);
   else
-    hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, false>), dim3((unsigned)l.blocks2), block, 0, stream, in, w, out);
+    hipLaunchKernelGGL((pass2_kernel<E, VEC, U2, false, FILT>), dim3((unsigned)l.blocks2), block, 0, stream, in, w,
+                       out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
   return hipSuccess;
@@ -1555,12 +2076,19 @@ hipError_t launch_sums(const Plan& p, Inputs in, const Work& w, float* out_min, 
   return hipGetLastError();
 }
 
+static FilterSide side_of(const sv_filter* f) {
+  return f ? FilterSide{f->top_k, f->top_p, f->min_p} : FilterSide{nullptr, nullptr, nullptr};
+}
+
+static bool any_filter(const FilterSide& f) { return f.top_k || f.top_p || f.min_p; }
+
 static sv_status run(const void* target, const void* draft, const int32_t* draft_tokens,
                      const int32_t* row_offsets, const float* temperature, const float* tau,
                      const float* tau_step, const float* min_cum,
                      uint64_t seed, int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
                      void* workspace, size_t workspace_bytes, void* hip_stream,
-                     sv_row_diag* diag, sv_batch_stats* stats, void* const* events) {
+                     sv_row_diag* diag, sv_batch_stats* stats, void* const* events,
+                     const sv_filter* tfilt = nullptr, const sv_filter* dfilt = nullptr) {
   Plan p;
   const sv_status st = check_call(shape, target, draft, draft_tokens, row_offsets, temperature, tau,
                                   out_tokens, out_accept_len, workspace, workspace_bytes, &p);
@@ -1582,6 +2110,25 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
                        (reinterpret_cast<uintptr_t>(draft) % 16) == 0;
   hipError_t err = counters_ready(p, ws, stream);
   if (err != hipSuccess) return SV_E_HIP;
+  const FilterSide ft = side_of(tfilt), fd = side_of(dfilt);
+  if (any_filter(ft) || any_filter(fd)) {
+    in.theta = reinterpret_cast<float*>(ws + p.off_theta);
+    in.filt[0] = ft;
+    in.filt[1] = fd;
+    const FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
+    if (p.dtype == SV_BF16) {
+      err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
+      if (err == hipSuccess)
+        err = aligned ? launch_pair<uint16_t, 8, true>(p, in, w, out, stream, ev)
+                      : launch_pair<uint16_t, 1, true>(p, in, w, out, stream, ev);
+    } else {
+      err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+      if (err == hipSuccess)
+        err = aligned ? launch_pair<float, 4, true>(p, in, w, out, stream, ev)
+                      : launch_pair<float, 1, true>(p, in, w, out, stream, ev);
+    }
+    return err == hipSuccess ? SV_OK : SV_E_HIP;
+  }
   if (p.dtype == SV_BF16) {
     err = aligned ? launch_pair<uint16_t, 8>(p, in, w, out, stream, ev)
                   : launch_pair<uint16_t, 1>(p, in, w, out, stream, ev);
@@ -1695,4 +2242,44 @@ extern "C" sv_status sv_verify_batch_sched(const void* target_logits, const void
   return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, tau_step, min_cum,
                  seed, out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
                  out_row_diag, out_stats, nullptr);
+}
+
+extern "C" sv_status sv_verify_batch_filtered(const void* target_logits, const void* draft_logits,
+                                              const int32_t* draft_tokens, const int32_t* row_offsets,
+                                              const float* temperature, const float* tau, const float* tau_step,
+                                              const float* min_cum, const sv_filter* target_filter,
+                                              const sv_filter* draft_filter, uint64_t seed, int32_t* out_tokens,
+                                              int32_t* out_accept_len, sv_shape shape, void* workspace,
+                                              size_t workspace_bytes, void* hip_stream, sv_row_diag* out_row_diag,
+                                              sv_batch_stats* out_stats) {
+  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, tau_step, min_cum,
+                 seed, out_tokens, out_accept_len, shape, workspace, workspace_bytes, hip_stream,
+                 out_row_diag, out_stats, nullptr, target_filter, draft_filter);
+}
+
+extern "C" sv_status sv_filter_thresholds(const void* target_logits, const void* draft_logits,
+                                          const int32_t* row_offsets, const float* temperature,
+                                          const sv_filter* target_filter, const sv_filter* draft_filter,
+                                          float* out_theta, sv_shape shape, void* workspace,
+                                          size_t workspace_bytes, void* hip_stream) {
+  using namespace sv;
+  Plan p;
+  const sv_status st = make_plan(shape, &p);
+  if (st != SV_OK) return st;
+  if (shape.B == 0) return SV_OK;
+  if (!target_logits || !draft_logits || !row_offsets || !temperature || !out_theta || !workspace)
+    return SV_E_NULLPTR;
+  if (workspace_bytes < p.total) return SV_E_WORKSPACE;
+  Inputs in{target_logits, draft_logits, nullptr, row_offsets, temperature, nullptr, nullptr, nullptr,
+            0, p.B, p.R, p.V, p.dtype, 1, 1};
+  const FilterArgs fa{{side_of(target_filter), side_of(draft_filter)}, out_theta};
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;
+  hipError_t err;
+  if (p.dtype == SV_BF16)
+    err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
+  else
+    err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+  return err == hipSuccess ? SV_OK : SV_E_HIP;
 }

@@ -65,9 +65,10 @@ struct P2Part {
   float mref;       // bonus rows: max target logit of the span
   int32_t bad;      // bonus rows: span holds NaN or +inf
   int32_t gidx;     // greedy bonus rows: lowest index of mref
-  int32_t pad;
+  int32_t pidx;     // filtered residual rows: best token of the race over p (-1 if none) ...
+  double pkey;      // ... and its fp64 key, the draw if the residual turns out to be empty
 };
-static_assert(sizeof(P2Part) == 32, "P2Part layout");
+static_assert(sizeof(P2Part) == 40, "P2Part layout");
 
 // Acceptance sums: one partial per (row, pass-1 wave) of sum min(p, mu) and sum p q.
 struct SumPart {
@@ -86,7 +87,7 @@ struct Plan {
   int32_t esize;  // bytes per logit
   int32_t w1max;  // pass 1: most waves that share one row (sizes the partial array)
   int32_t w2max;  // pass 2: most waves that share one request
-  size_t off_hdr, off_part1, off_part2, off_part3, off_lazy, off_ticket2, off_done3, total;
+  size_t off_hdr, off_part1, off_part2, off_part3, off_lazy, off_theta, off_ticket2, off_done3, total;
 };
 
 // Build the plan for a shape. Returns SV_OK, or the status describing why the

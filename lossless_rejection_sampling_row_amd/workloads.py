@@ -215,3 +215,22 @@ def config(cfg: int, verify_seed: int | None = None, rng_seed: int | None = None
     if rng_seed is not None:
         spec = replace(spec, rng_seed=int(rng_seed))
     return generate(spec)
+
+
+def sampler_filters(B: int, rng_seed: int = 0):
+    """A serving-style sampler configuration per request, for the target and for the draft.
+
+    Each side gets its own (top_k [B] int32, top_p [B] float32, min_p [B] float32), drawn
+    from values common in serving: top_k in {0 (off), 20, 50}, top_p in {1 (off), 0.9,
+    0.95}, min_p in {0 (off), 0.05}. The drafted tokens stay those of the unfiltered
+    drafter.
+    """
+    rng = np.random.default_rng(rng_seed)
+
+    def side():
+        return (rng.choice([0, 20, 50], size=B).astype(np.int32),
+                rng.choice([1.0, 0.9, 0.95], size=B).astype(np.float32),
+                rng.choice([0.0, 0.05], size=B).astype(np.float32))
+
+    return side(), side()
+

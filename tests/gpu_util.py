@@ -46,6 +46,12 @@ def upload(batch, device="cuda"):
     for key in ("tau_step", "min_cum"):  # optional gate schedule and cumulative floor
         if batch.get(key) is not None:
             g[key] = torch.from_numpy(np.ascontiguousarray(batch[key], dtype=np.float32)).to(device)
+    for key in ("target_filter", "draft_filter"):  # optional (top_k, top_p, min_p) triples
+        f = batch.get(key)
+        if f is not None:
+            g[key] = tuple(None if a is None else
+                           torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32 if i == 0 else np.float32)).to(device)
+                           for i, a in enumerate(f))
     return g
 
 
@@ -72,7 +78,8 @@ def run_gpu(batch, seed=None, gpu=None, diag=True):
     toks, lens = binding.verify_batch(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"],
                                       g["temperature"], g["tau"], batch["seed"] if seed is None else seed,
                                       row_diag=row_diag, stats=stats, tau_step=g.get("tau_step"),
-                                      min_cum=g.get("min_cum"))
+                                      min_cum=g.get("min_cum"), target_filter=g.get("target_filter"),
+                                      draft_filter=g.get("draft_filter"))
     torch.cuda.synchronize()
     if diag:
         p, q, mu, u, rm, v = binding.split_row_diag(row_diag)
@@ -87,7 +94,8 @@ def run_oracle(batch, seed=None, requests=None):
     return ov.verify_batch(batch["target"], batch["draft"], batch["draft_tokens"], batch["row_offsets"],
                            batch["temperature"], batch["tau"], batch["seed"] if seed is None else seed,
                            batch["dtype"], requests=requests, tau_step=batch.get("tau_step"),
-                           min_cum=batch.get("min_cum"))
+                           min_cum=batch.get("min_cum"), target_filter=batch.get("target_filter"),
+                           draft_filter=batch.get("draft_filter"))
 
 
 @dataclass

@@ -40,7 +40,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"sv_verify_batch", "sv_verify_batch_diag", "sv_verify_batch_sched", "sv_verify_batch_lazy",
-                          "sv_row_acceptance", "sv_workspace_bytes",
+                          "sv_row_acceptance", "sv_verify_batch_filtered", "sv_filter_thresholds",
+                          "sv_workspace_bytes",
                           "sv_status_string", "sv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -113,6 +114,7 @@ int main() {
   const void* v = dummy;
   CHECK(make_plan(sv_shape{64, 320, 151936, SV_BF16}, &p) == SV_OK);
   CHECK(p.w1max == 64 && p.w2max == 64 && p.total % 256 == 0 && p.off_ticket2 < p.total);
+  CHECK(p.off_theta % 256 == 0 && p.off_theta >= p.off_lazy + 64 * 4 && p.off_theta + 320 * 8 <= p.off_ticket2);
   {
     const Launch l = pick_waves(p, 1536, 1536);  // six waves per CU on 256 CUs
     CHECK(l.w1 == 4 && l.w2 == 24 && l.blocks1 == 256 * 4 / 4 && l.blocks2 == 64 * 24 / 4);

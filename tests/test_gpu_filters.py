@@ -1,0 +1,273 @@
+"""GPU parity of the filtered verify (top-k, top-p, min-p on p and q) against the oracle.
+
+mlxcel PR #992, section What changed: the sampler's filter chain defines the
+effective p and q. The bars:
+
+* Keep-thresholds (sv_filter_thresholds): the kept set of every row must
+  equal the oracle's exactly, except on rows where a top-p or min-p decision
+  falls within the oracle's flag band. Greedy and unfiltered rows get -inf,
+  and invalid rows get +inf.
+* Verify (sv_verify_batch_filtered): the bar of the other parity tests.
+  Tokens, accept lengths and verdicts are bit-exact outside flagged requests;
+  p(D), q(D) and mu(D) agree to 1e-5 relative; the residual mass agrees to
+  max(1e-5 R, 2e-6). Both the diagnostic and the plain kernel are checked.
+* The page's zero-tolerance property (section Where chi-square is blind): a
+  top_k = 2 target against an unfiltered drafter never emits a token outside
+  the target's two-token support.
+* With every filter off, the filtered call returns exactly what the
+  unfiltered call returns.
+
+The drafted tokens come from the unfiltered draft distribution, as in the
+page's support test. So a filtered q may give q(D) = 0.
+"""
+import numpy as np
+import pytest
+
+from lossless_rejection_sampling_row_amd import workloads as wl
+from oracle import filters as of
+from oracle import verify as ov
+from tests.gpu_util import Parity, as_batch, check_properties, compare, run_gpu, run_oracle, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_rejection_sampling_row_amd import binding
+    binding.load_library()
+    yield
+
+
+def random_filters(B, V, rng, ks=None, tps=None, mps=None):
+    ks = [0, 1, 2, 5, 50, 500, V] if ks is None else ks
+    tps = [1.0, 0.3, 0.8, 0.9, 0.95, 0.99] if tps is None else tps
+    mps = [0.0, 0.0, 0.01, 0.05, 0.2] if mps is None else mps
+    return (rng.choice(ks, size=B).astype(np.int32), rng.choice(tps, size=B).astype(np.float32),
+            rng.choice(mps, size=B).astype(np.float32))
+
+
+def oracle_thresholds(batch, side):
+    """Per row: (theta or None when no filter applies, near)."""
+    ro = np.asarray(batch["row_offsets"], dtype=np.int64)
+    temp = np.asarray(batch["temperature"], dtype=np.float32).astype(np.float64)
+    arr = batch["target" if side == 0 else "draft"]
+    trip = batch["target_filter" if side == 0 else "draft_filter"]
+    out = []
+    for b in range(ro.size - 1):
+        f = ov.request_filter(trip, b)
+        for r in range(int(ro[b]), int(ro[b + 1])):
+            x = ov.decode_logits(arr[r], batch["dtype"])
+            if f is None or temp[b] == 0.0 or not of.filter_valid(f) or not of.filter_active(f, x.size):
+                out.append((None, False))
+            elif not ov.row_valid(x):
+                out.append((np.inf, False))
+            else:
+                out.append(of.threshold(x, float(temp[b]), f))
+    return out
+
+
+def check_thresholds(batch, label):
+    import torch
+    from lossless_rejection_sampling_row_amd import binding
+    g = upload(batch)
+    th = binding.filter_thresholds(g["target"], g["draft"], g["row_offsets"], g["temperature"],
+                                   target_filter=g.get("target_filter"), draft_filter=g.get("draft_filter"))
+    torch.cuda.synchronize()
+    th = th.cpu().numpy().astype(np.float64)
+    checked = near_rows = 0
+    for side in (0, 1):
+        arr = batch["target" if side == 0 else "draft"]
+        for r, (want, near) in enumerate(oracle_thresholds(batch, side)):
+            got = th[r, side]
+            ctx = f"{label} side={side} row={r} gpu theta={got!r} oracle={want!r}"
+            if want is None:
+                assert got == -np.inf, ctx
+                continue
+            if want == np.inf:
+                assert got == np.inf, ctx
+                continue
+            if near:
+                near_rows += 1
+                continue
+            x = ov.decode_logits(arr[r], batch["dtype"])
+            assert np.array_equal(x >= got, x >= want), ctx + f" kept gpu {(x >= got).sum()} oracle {(x >= want).sum()}"
+            checked += 1
+    say(f"[filters] thresholds {label}: {checked} rows equal, {near_rows} near-boundary rows skipped")
+    return checked, near_rows
+
+
+def _spec(V, dtype, B=24, spikes=True, seed=0, **kw):
+    return wl.Spec(B=B, T=(1, 6), V=V, dtype=dtype, sigma_t=3.0, n_spikes=min(8, V // 4) if spikes else 0,
+                   sigma_d=(0.5, 2.0), temperature=(0.5, 1.2), greedy_frac=0.1, tau=(0.0, 0.1, 0.3),
+                   noprop_frac=0.05, rng_seed=seed, verify_seed=seed, **kw)
+
+
+@pytest.mark.parametrize("V,dtype,spikes", [(37, "f32", True), (4096, "bf16", True), (12289, "f32", False),
+                                            (32000, "bf16", True), (32000, "bf16", False)])
+def test_thresholds_match_oracle(V, dtype, spikes):
+    batch = as_batch(wl.generate(_spec(V, dtype, spikes=spikes, seed=300 + V)))
+    rng = np.random.default_rng(V)
+    B = len(batch["tau"])
+    batch["target_filter"] = random_filters(B, V, rng)
+    batch["draft_filter"] = random_filters(B, V, rng)
+    checked, near = check_thresholds(batch, f"V={V} {dtype} spikes={spikes}")
+    assert checked > 0 and near <= 0.02 * checked + 2
+
+
+def test_thresholds_exact_fallback_paths():
+    # Flat rows: more logits than the candidate store within half a log2 unit of the maximum,
+    # so top-k (k = 9000) and top-p (0.99) are decided by bisection over the whole row.
+    rng = np.random.default_rng(4)
+    V, B = 20000, 4
+    spec = wl.Spec(B=B, T=2, V=V, dtype="f32", sigma_t=0.05, temperature=1.0, rng_seed=77, verify_seed=1)
+    batch = as_batch(wl.generate(spec))
+    batch["target_filter"] = (np.array([9000, 0, 9000, 3], np.int32), np.array([1.0, 0.99, 0.6, 0.5], np.float32),
+                              None)
+    batch["draft_filter"] = (None, np.array([0.7, 0.999, 1.0, 0.2], np.float32),
+                             np.array([0.0, 0.0, 0.97, 0.0], np.float32))
+    checked, _ = check_thresholds(batch, "flat V=20000")
+    assert checked >= 10
+    # every logit equal: ties everywhere, the top bin overflows the candidate store
+    tie = np.zeros((3, 9000), dtype=np.float32) + 1.25
+    from tests.helpers import batch_from_rows
+    b2 = batch_from_rows(tie, tie, [0, 1, -1], [0, 3], [1.0], [0.0])
+    b2["target_filter"] = (np.array([5], np.int32), np.array([0.5], np.float32), np.array([0.9], np.float32))
+    b2["draft_filter"] = (np.array([1], np.int32), None, None)
+    c2, _ = check_thresholds(b2, "all ties")
+    assert c2 == 6
+
+
+def test_thresholds_invalid_rows_and_greedy():
+    from tests.helpers import batch_from_rows
+    rng = np.random.default_rng(8)
+    t = rng.normal(0, 2, size=(6, 500)).astype(np.float32)
+    d = rng.normal(0, 2, size=(6, 500)).astype(np.float32)
+    t[1, 7] = np.nan
+    d[4, :] = -np.inf
+    b = batch_from_rows(t, d, [1, 2, -1, 3, 4, -1], [0, 3, 6], [1.0, 0.0], [0.0, 0.0])
+    b["target_filter"] = (np.array([3, 3], np.int32), None, None)
+    b["draft_filter"] = (None, np.array([0.9, 0.9], np.float32), None)
+    check_thresholds(b, "invalid and greedy")
+
+
+def _verify_parity(batch, seeds, label):
+    tot = Parity()
+    g = upload(batch)
+    for s in seeds:
+        say(f"[filters] verify {label} seed={s}")
+        gpu = run_gpu(batch, seed=s, gpu=g)
+        fast = run_gpu(batch, seed=s, gpu=g, diag=False)
+        ora = run_oracle(batch, seed=s)
+        tot.add(compare(batch, gpu, ora))
+        compare(batch, fast, ora, check_diag=False)
+    say(f"[filters] verify {label}: {tot}")
+    return tot
+
+
+@pytest.mark.parametrize("V,dtype,spikes", [(64, "bf16", True), (4097, "f32", True), (16384, "bf16", False),
+                                            (40000, "bf16", True)])
+def test_filtered_verify_matches_oracle(V, dtype, spikes):
+    batch = as_batch(wl.generate(_spec(V, dtype, B=32, spikes=spikes, seed=500 + V)))
+    rng = np.random.default_rng(V + 1)
+    B = len(batch["tau"])
+    batch["target_filter"] = random_filters(B, V, rng)
+    batch["draft_filter"] = random_filters(B, V, rng)
+    tot = _verify_parity(batch, range(5), f"V={V} {dtype} spikes={spikes}")
+    assert tot.flagged_requests <= 0.05 * tot.requests + 2
+
+
+def test_filtered_verify_with_schedule_and_one_side():
+    batch = as_batch(wl.generate(_spec(8192, "bf16", B=40, seed=61)))
+    rng = np.random.default_rng(61)
+    B = len(batch["tau"])
+    from lossless_rejection_sampling_row_amd import binding
+    batch["tau_step"] = binding.expand_schedule([0.0, 0.05, 0.2], batch["row_offsets"])
+    batch["min_cum"] = np.full(B, 1e-3, dtype=np.float32)
+    batch["target_filter"] = (None, random_filters(B, 8192, rng)[1], None)   # top-p only, target only
+    _verify_parity(batch, range(3), "top-p target only, schedule")
+    batch["target_filter"] = None
+    batch["draft_filter"] = (random_filters(B, 8192, rng)[0], None, np.full(B, 0.05, np.float32))
+    _verify_parity(batch, range(3), "draft top-k + min-p only, schedule")
+
+
+def test_filtered_target_support_is_never_violated():
+    import torch
+    V, n_draft, n_req = 64, 3, 600
+    spec = wl.Spec(B=n_req, T=n_draft, V=V, dtype="f32", sigma_t=1.5, sigma_d=1.5, temperature=1.0,
+                   rng_seed=12, verify_seed=3)
+    batch = as_batch(wl.generate(spec))
+    batch["target_filter"] = (np.full(n_req, 2, np.int32), None, None)
+    emitted = outside = 0
+    g = upload(batch)
+    for s in range(3):
+        gpu = run_gpu(batch, seed=s, gpu=g, diag=False)
+        check_properties(batch, gpu)
+        ro = batch["row_offsets"]
+        for b in range(n_req):
+            k = int(gpu.out_accept_len[b])
+            assert k >= 0
+            for j in range(k + 1):
+                row = batch["target"][ro[b] + j].astype(np.float64)
+                top2 = set(np.argsort(-row, kind="stable")[:2].tolist())
+                emitted += 1
+                outside += int(gpu.out_tokens[ro[b] + j]) not in top2
+    say(f"[filters] support: {emitted} emitted tokens, {outside} outside the target's top-2")
+    assert emitted >= 1500 and outside == 0
+
+
+def test_filters_off_equal_the_unfiltered_call():
+    batch = as_batch(wl.generate(_spec(12288, "bf16", B=32, seed=71)))
+    B = len(batch["tau"])
+    g = upload(batch)
+    plain = run_gpu(batch, seed=5, gpu=g)
+    off = dict(batch)
+    off["target_filter"] = (np.zeros(B, np.int32), np.ones(B, np.float32), np.zeros(B, np.float32))
+    off["draft_filter"] = (np.full(B, 12288, np.int32), np.full(B, 1.5, np.float32), None)
+    got = run_gpu(off, seed=5, gpu=upload(off))
+    assert np.array_equal(got.out_tokens, plain.out_tokens)
+    assert np.array_equal(got.out_accept_len, plain.out_accept_len)
+    assert np.array_equal(got.verdict, plain.verdict)
+    tested = plain.verdict > 0
+    assert np.array_equal(got.p_D[tested], plain.p_D[tested], equal_nan=True)
+
+
+def test_invalid_filter_values_fail_the_request():
+    batch = as_batch(wl.generate(_spec(2048, "f32", B=12, seed=81)))
+    B = len(batch["tau"])
+    temp = np.asarray(batch["temperature"])
+    k = np.zeros(B, np.int32)
+    tp = np.ones(B, np.float32)
+    mp = np.zeros(B, np.float32)
+    k[0], tp[1], tp[2], mp[3], mp[4] = -1, 0.0, np.nan, 1.5, np.nan
+    batch["target_filter"] = (k, tp, None)
+    batch["draft_filter"] = (None, None, mp)
+    gpu = run_gpu(batch, seed=2)
+    ora = run_oracle(batch, seed=2)
+    compare(batch, gpu, ora)
+    for b in range(5):
+        assert gpu.out_accept_len[b] == (-1 if temp[b] > 0 else ora.out_accept_len[b])
+
+
+def test_gated_batch_full_size_sampled():
+    # The gated workload at its full size (B=64, T=4, V=151936, bf16) with a sampler
+    # configuration on both sides. The oracle checks a sample of requests; every request
+    # is checked for the output invariants.
+    batch = as_batch(wl.config(3))
+    B = len(batch["tau"])
+    rng = np.random.default_rng(3)
+    batch["target_filter"] = (rng.choice([0, 20, 50], size=B).astype(np.int32),
+                              rng.choice([1.0, 0.9, 0.95], size=B).astype(np.float32),
+                              rng.choice([0.0, 0.05], size=B).astype(np.float32))
+    batch["draft_filter"] = (rng.choice([0, 50], size=B).astype(np.int32),
+                             rng.choice([1.0, 0.95], size=B).astype(np.float32), None)
+    g = upload(batch)
+    gpu = run_gpu(batch, seed=9, gpu=g)
+    check_properties(batch, gpu)
+    sample = list(range(0, B, 5))
+    ora = run_oracle(batch, seed=9, requests=sample)
+    par = compare(batch, gpu, ora, requests=sample)
+    say(f"[filters] full-size sample: {par}")
+    assert par.requests == len(sample)

@@ -1558,6 +1558,8 @@ __global__ __launch_bounds__(kBlock) void merge_sums_kernel(Inputs in, Work w, f
 //    are decided by bisection over the float order, one pass over the row per step: top-k
 //    on counts (after which top-k's set is gathered for top-p when it fits), top-p on fp64
 //    masses. Exact; the second is slow. Peaked rows keep the window small.
+constexpr int kFiltBlock = 512;  // threads per (row, side): 2 workgroups per CU fit
+constexpr int kFiltWaves = kFiltBlock / kWave;
 constexpr int kCandCap = 8192;  // candidate logits one workgroup sorts in LDS
 
 // Total order on non-NaN floats as int32: order_key(a) < order_key(b) iff a < b, with -0
@@ -1570,7 +1572,7 @@ __device__ __forceinline__ float key_float(int32_t k) { return __int_as_float(k 
 
 struct FilterSmem {
   float cand[kCandCap];
-  double red[kWavesPerBlock];
+  double red[kFiltWaves];
   int n_cand, first;
 };
 
@@ -1581,7 +1583,7 @@ __device__ __forceinline__ double block_sum(double v, FilterSmem& s) {
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) t += s.red[w];
+  for (int w = 0; w < kFiltWaves; ++w) t += s.red[w];
   return t;
 }
 
@@ -1592,13 +1594,13 @@ __device__ __forceinline__ float block_max(float v, FilterSmem& s) {
   __syncthreads();
   float t = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) t = fmaxf(t, (float)s.red[w]);
+  for (int w = 0; w < kFiltWaves; ++w) t = fmaxf(t, (float)s.red[w]);
   return t;
 }
 
 // Walk a row with every thread of the workgroup: step st covers vectors
-// [st * kBlock * kFiltLoads, (st + 1) * kBlock * kFiltLoads), kFiltLoads per thread, strided
-// by kBlock. Every lane runs every step (a lane past the row's end re-reads the row's last
+// [st * kFiltBlock * kFiltLoads, (st + 1) * kFiltBlock * kFiltLoads), kFiltLoads per thread, strided
+// by kFiltBlock. Every lane runs every step (a lane past the row's end re-reads the row's last
 // vector, a cache hit, and sees ok = false), so the step function may use wave-wide
 // operations. Loads are double-buffered: the next step's vectors are in flight while
 // step(x, ok, st) works on the current ones.
@@ -1607,17 +1609,17 @@ constexpr int kFiltLoads = 4;
 template <typename E, int VEC, class S>
 __device__ __forceinline__ void walk_row(const E* row, int nvec, S step) {
   using CH = Chunk<E, VEC>;
-  constexpr int per = kBlock * kFiltLoads;
+  constexpr int per = kFiltBlock * kFiltLoads;
   const int steps = (nvec + per - 1) / per;
   auto load = [&](CH (&x)[kFiltLoads], int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kFiltLoads; ++u)
-      x[u].load(row + (int64_t)min(st * per + u * kBlock + (int)threadIdx.x, nvec - 1) * VEC);
+      x[u].load(row + (int64_t)min(st * per + u * kFiltBlock + (int)threadIdx.x, nvec - 1) * VEC);
   };
   auto run = [&](const CH (&x)[kFiltLoads], int st) __attribute__((always_inline)) {
     bool ok[kFiltLoads];
 #pragma unroll
-    for (int u = 0; u < kFiltLoads; ++u) ok[u] = st * per + u * kBlock + (int)threadIdx.x < nvec;
+    for (int u = 0; u < kFiltLoads; ++u) ok[u] = st * per + u * kFiltBlock + (int)threadIdx.x < nvec;
     step(x, ok, st);
   };
   CH xa[kFiltLoads], xb[kFiltLoads];
@@ -1677,7 +1679,7 @@ __device__ float bisect_float(float lo, float hi, P pred) {
 }
 
 template <typename E, int VEC>
-__global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArgs fa) {
+__global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, FilterArgs fa) {
   __shared__ FilterSmem s;
   const int r = blockIdx.x;
   const int side = blockIdx.y;
@@ -1713,11 +1715,11 @@ __global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArg
   auto sort_desc = [&](int n) __attribute__((always_inline)) {
     int np2 = 1;
     while (np2 < n) np2 <<= 1;
-    for (int i = n + threadIdx.x; i < np2; i += kBlock) s.cand[i] = -INFINITY;
+    for (int i = n + threadIdx.x; i < np2; i += kFiltBlock) s.cand[i] = -INFINITY;
     __syncthreads();
     for (int k = 2; k <= np2; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = threadIdx.x; i < np2; i += kBlock) {
+        for (int i = threadIdx.x; i < np2; i += kFiltBlock) {
           const int ij = i ^ j;
           if (ij > i) {
             const float a = s.cand[i], z = s.cand[ij];
@@ -1760,21 +1762,21 @@ __global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArg
   }
 
   // ---- the candidates to gather
-  //  - With top-k (k <= kBlock): the logits at or above the k-th largest of the threads'
+  //  - With top-k (k <= kFiltBlock): the logits at or above the k-th largest of the threads'
   //    maxima. At least k logits reach it, so it is at most top-k's threshold; and top-p's
   //    crossing lies above top-k's threshold.
   //  - With top-p alone: the logits within W = log2(V / (1 - top_p)) + 1 log2 units of mass
   //    below the maximum. A logit below that has mass under 2^-W of the maximum's, so all of
   //    them together hold less than V * 2^-W < (1 - top_p) of the row's mass (which holds
   //    the maximum): the crossing lies inside.
-  //  - With top-k beyond kBlock alone: a 24-unit window, a guess checked below.
+  //  - With top-k beyond kFiltBlock alone: a 24-unit window, a guess checked below.
   const float c = scale_of(T);  // log2(e) / T
   const float W = topp ? log2f((float)in.V / (1.0f - fp.top_p)) + 1.0f : 24.0f;
   float edge = -INFINITY;
-  const bool by_edge = topk && fp.k <= kBlock;
+  const bool by_edge = topk && fp.k <= kFiltBlock;
   if (by_edge) {
     s.cand[threadIdx.x] = mx;  // -inf for a thread that read nothing
-    sort_desc(kBlock);
+    sort_desc(kFiltBlock);
     edge = s.cand[fp.k - 1];
     __syncthreads();
   }
@@ -1827,7 +1829,7 @@ __global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArg
   // fp64 mass plus `extra` (the mass of top-k's set outside them). Returns the logit at the
   // first position whose prefix mass reaches top_p * S1, or NaN when the candidates hold less.
   auto top_p_scan = [&](int nk, double extra) __attribute__((always_inline)) {
-    const int ch = (nk + kBlock - 1) / kBlock;
+    const int ch = (nk + kFiltBlock - 1) / kFiltBlock;
     const int i0 = min((int)threadIdx.x * ch, nk), i1 = min(i0 + ch, nk);
     double own = 0.0;
     for (int i = i0; i < i1; ++i) own += exp(((double)s.cand[i] - (double)m) / Td);
@@ -1842,7 +1844,7 @@ __global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArg
     __syncthreads();
     double before = 0.0, total = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
+    for (int w = 0; w < kFiltWaves; ++w) {
       before += w < wave ? s.red[w] : 0.0;
       total += s.red[w];
     }
@@ -1865,7 +1867,7 @@ __global__ __launch_bounds__(kBlock) void thresholds_kernel(Inputs in, FilterArg
   auto count_prefix = [&](int n, int k, float th) __attribute__((always_inline)) {
     if (threadIdx.x == 0) s.first = n;
     __syncthreads();
-    for (int i = k - 1 + threadIdx.x; i < n - 1; i += kBlock)
+    for (int i = k - 1 + threadIdx.x; i < n - 1; i += kFiltBlock)
       if (s.cand[i + 1] < th) atomicMin(&s.first, i + 1);
     __syncthreads();
     const int nk = s.first;
@@ -1992,7 +1994,7 @@ static hipError_t resident_waves(const void* fn, int per_cu_target, int64_t* slo
 // and side.
 template <typename E, int VEC>
 hipError_t launch_thresholds(const Plan& p, const Inputs& in, const FilterArgs& fa, hipStream_t stream) {
-  hipLaunchKernelGGL((thresholds_kernel<E, VEC>), dim3((unsigned)p.R, 2u), dim3(kBlock), 0, stream, in, fa);
+  hipLaunchKernelGGL((thresholds_kernel<E, VEC>), dim3((unsigned)p.R, 2u), dim3(kFiltBlock), 0, stream, in, fa);
   return hipGetLastError();
 }
 

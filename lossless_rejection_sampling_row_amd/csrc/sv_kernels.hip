@@ -467,17 +467,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)rg * in.V;
   const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)rg * in.V;
   CH ta[U], da[U];
-  // The first batch of the guessed row is requested before the slot is classified, so the
-  // row's metadata and its first logits arrive together.
+  // The first batch of the guessed row (and, filtered, its keep-thresholds) is requested
+  // before the slot is classified, so the row's metadata and its first logits arrive together.
   if (sp.begin < sp.end) {
     load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
     load_chunks<true>(da, drow, sp.begin, lane, sp.end);
   }
+  float th_t = -INFINITY, th_d = -INFINITY;
+  if (FILT) {
+    th_t = in.theta[2 * (int64_t)rg];
+    th_d = in.theta[2 * (int64_t)rg + 1];
+  }
   const RowCls cls = classify_slot(in, p, bg, lane);
   if (!cls.proposal) return;
   const int r = cls.r;
-  float th_t = -INFINITY, th_d = -INFINITY;
-  if (FILT) {
+  if (FILT && r != rg) {
     th_t = in.theta[2 * (int64_t)r];
     th_d = in.theta[2 * (int64_t)r + 1];
   }
@@ -1598,12 +1602,12 @@ __device__ __forceinline__ float block_max(float v, FilterSmem& s) {
   return t;
 }
 
-// Walk a row with every thread of the workgroup: step st covers vectors
-// [st * kFiltBlock * kFiltLoads, (st + 1) * kFiltBlock * kFiltLoads), kFiltLoads per thread, strided
-// by kFiltBlock. Every lane runs every step (a lane past the row's end re-reads the row's last
-// vector, a cache hit, and sees ok = false), so the step function may use wave-wide
-// operations. Loads are double-buffered: the next step's vectors are in flight while
-// step(x, ok, st) works on the current ones.
+// Walk a row with every thread of the workgroup: step st covers the kFiltBlock * kFiltLoads
+// vectors from st * kFiltBlock * kFiltLoads on, kFiltLoads per thread, strided by kFiltBlock.
+// Every lane runs every step (a lane past the row's end re-reads the row's last vector, a
+// cache hit, and sees ok = false), so the step function may use wave-wide operations. Loads
+// are double-buffered: the next step's vectors are in flight while step(x, ok, st) works on
+// the current ones.
 constexpr int kFiltLoads = 4;
 
 template <typename E, int VEC, class S>
@@ -1784,11 +1788,11 @@ __global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, Filte
   // below m - W / c, so that fp32 rounding can only widen it.
   const float lo = by_edge ? edge : m - (W + 0.01f) / c;
   // ---- gather, sort, scan
-  // gather(lo, ...): the logits >= lo go to s.cand. Returns how many there are (those past
-  // kCandCap are counted, not stored).
-  // Per step each lane counts its candidates and, holding any, reserves their slots with one
-  // LDS atomic and stores them. With sum_rest, the fp32 mass of the
-  // other logits goes to `rest` (per vector in fp32, per lane in fp64).
+  // gather(bound, ...): the logits >= the bound go to s.cand. Returns how many there are
+  // (those past kCandCap are counted, not stored). Per step each lane counts its candidates
+  // and, holding any, reserves their slots with one LDS atomic and stores them. With
+  // sum_rest, the fp32 mass of the other logits goes to `rest` (per vector in fp32, per lane
+  // in fp64).
   auto gather = [&](const float lo, const bool sum_rest, double& rest) __attribute__((always_inline)) {
     if (threadIdx.x == 0) s.n_cand = 0;
     __syncthreads();

@@ -67,3 +67,31 @@ def test_row_counts():
     assert bench.tested_rows(w, np.array([3, -1])) == 3
     # final-row bytes: request 0 stops at a residual row (both arrays), request 1 at a bonus row
     assert bench.pass2_bytes(w, np.array([1, 1]), 2) == 2 * 8 * 2 + 8 * 2
+
+
+def test_filtered_row_counts():
+    # three requests of 2, 3 and 1 rows; request 1 is greedy (its filters never apply)
+    w = _W([0, 2, 5, 6], [1, -1, 2, 3, -1, -1], 10, [1.0, 0.0, 0.7])
+    k = np.array([3, 3, 0], dtype=np.int32)
+    tp = np.array([1.0, 1.0, 1.0], dtype=np.float32)
+    mp = np.array([0.0, 0.0, 0.0], dtype=np.float32)
+    assert bench.filtered_rows(w, (k, tp, mp)) == 2            # top-k on request 0 only
+    mp[2] = 0.05
+    assert bench.filtered_rows(w, (k, tp, mp)) == 3            # min-p turns request 2 on
+    k[0] = 10                                                  # k >= V is off
+    assert bench.filtered_rows(w, (k, tp, mp)) == 1
+    tp[0] = 0.9
+    assert bench.filtered_rows(w, (k, tp, mp)) == 3
+
+
+def test_sampler_filter_recipe():
+    from lossless_rejection_sampling_row_amd import workloads as wl
+    t1, d1 = wl.sampler_filters(64, rng_seed=7)
+    t2, d2 = wl.sampler_filters(64, rng_seed=7)
+    for a, b in zip(t1 + d1, t2 + d2):
+        assert np.array_equal(a, b)
+    for k, tp, mp in (t1, d1):
+        assert k.dtype == np.int32 and tp.dtype == np.float32 and mp.dtype == np.float32
+        assert set(k.tolist()) <= {0, 20, 50} and set(tp.tolist()) <= {1.0, np.float32(0.9), np.float32(0.95)}
+        assert set(mp.tolist()) <= {0.0, np.float32(0.05)}
+    assert not all(np.array_equal(a, b) for a, b in zip(t1, d1))  # the two sides are drawn apart

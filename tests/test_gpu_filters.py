@@ -118,8 +118,8 @@ def test_thresholds_match_oracle(V, dtype, spikes):
 
 
 def test_thresholds_exact_fallback_paths():
-    # Flat rows: more logits than the candidate store within half a log2 unit of the maximum,
-    # so top-k (k = 9000) and top-p (0.99) are decided by bisection over the whole row.
+    # Flat rows: top-k's k = 9000 is beyond the threads'-maxima bound, and top-p's window holds
+    # more logits than the candidate store, so both are decided by bisection over the row.
     rng = np.random.default_rng(4)
     V, B = 20000, 4
     spec = wl.Spec(B=B, T=2, V=V, dtype="f32", sigma_t=0.05, temperature=1.0, rng_seed=77, verify_seed=1)
@@ -270,4 +270,22 @@ def test_gated_batch_full_size_sampled():
     ora = run_oracle(batch, seed=9, requests=sample)
     par = compare(batch, gpu, ora, requests=sample)
     say(f"[filters] full-size sample: {par}")
+    assert par.requests == len(sample)
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_other_full_size_workloads_sampled(cfg):
+    # Config 2 (B=32, V=128256, bf16) and config 5 (B=512, V=152064, fp32, greedy and
+    # no-proposal cohorts) at full size, with the serving recipe on both sides. The oracle
+    # checks a sample of requests; every request is checked for the output invariants.
+    batch = as_batch(wl.config(cfg))
+    B = len(batch["tau"])
+    batch["target_filter"], batch["draft_filter"] = wl.sampler_filters(B, rng_seed=100 + cfg)
+    g = upload(batch)
+    gpu = run_gpu(batch, seed=21, gpu=g)
+    check_properties(batch, gpu)
+    sample = list(range(0, B, max(1, B // 16)))
+    ora = run_oracle(batch, seed=21, requests=sample)
+    par = compare(batch, gpu, ora, requests=sample)
+    say(f"[filters] config {cfg} full-size sample: {par}")
     assert par.requests == len(sample)

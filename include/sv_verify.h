@@ -123,7 +123,9 @@ typedef struct sv_batch_stats {
  *          0 turns it off; NaN, < 0 or > 1 is invalid.
  * The kept set is the tokens at or above the largest of the three
  * thresholds, and p (or q) is the softmax over it. Filters apply only to
- * requests with T > 0; greedy requests ignore them and their values.
+ * requests with T > 0; greedy requests ignore them and their values. The
+ * emitted tokens follow the filtered p when each drafted token was drawn from
+ * the q the verifier uses, filtered or not.
  */
 typedef struct sv_filter {
   const int32_t* top_k;

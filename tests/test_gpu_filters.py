@@ -289,3 +289,39 @@ def test_other_full_size_workloads_sampled(cfg):
     par = compare(batch, gpu, ora, requests=sample)
     say(f"[filters] config {cfg} full-size sample: {par}")
     assert par.requests == len(sample)
+
+
+def test_gpu_stream_follows_the_filtered_target_law():
+    # Losslessness end to end on the GPU: 12000 identical windows (one draft, then the bonus
+    # row) with filters on both sides. The drafter samples its own filtered q, the q the
+    # verifier uses (with an unfiltered drafter against a filtered q the method is not
+    # lossless, and the oracle computes the same biased stream). The first emitted token must
+    # follow the filtered target law (scipy's softmax over the kept logits), chi-square at
+    # alpha 1e-4.
+    from scipy.special import softmax as sp_softmax
+    from tests.helpers import batch_from_rows, chi2_threshold, chi_square
+    V, T, n_req = 6, 0.9, 12000
+    t_log = np.array([2.0, 1.5, 1.2, 0.3, -0.4, -1.0], dtype=np.float32)
+    d_log = np.array([0.5, 1.9, 1.0, 1.1, 0.2, -0.3], dtype=np.float32)
+    t64 = t_log.astype(np.float64)
+    kept = t64 >= np.sort(t64)[::-1][3]                      # top-k = 4 keeps tokens 0..3
+    pk = np.where(kept, sp_softmax(np.where(kept, t64 / T, -np.inf)), 0.0)
+    order = np.argsort(-t64)
+    n_keep = int(np.argmax(np.cumsum(pk[order]) >= 0.95)) + 1   # then top-p 0.95
+    law = np.zeros(V)
+    law[order[:n_keep]] = sp_softmax(t64[order[:n_keep]] / T)
+    rng = np.random.default_rng(17)
+    q_draw, _ = ov.row_distribution(d_log.astype(np.float64), T, of.Filter(top_p=0.9, min_p=0.1))
+    toks = rng.choice(V, size=2 * n_req, p=q_draw)           # the drafter's filtered q
+    toks[1::2] = -1
+    batch = batch_from_rows(np.tile(t_log, (2 * n_req, 1)), np.tile(d_log, (2 * n_req, 1)), toks,
+                            np.arange(0, 2 * n_req + 1, 2), np.full(n_req, T), np.full(n_req, 0.05))
+    batch["target_filter"] = (np.full(n_req, 4, np.int32), np.full(n_req, 0.95, np.float32), None)
+    batch["draft_filter"] = (None, np.full(n_req, 0.9, np.float32), np.full(n_req, 0.1, np.float32))
+    gpu = run_gpu(batch, seed=31, diag=False)
+    first = gpu.out_tokens[0::2].astype(np.int64)
+    assert (gpu.out_accept_len >= 0).all()
+    stat = chi_square(first, law)
+    thr = chi2_threshold(int(np.count_nonzero(law)) - 1, 1e-4)
+    say(f"[filters] GPU chi-square {stat:.2f} against {thr:.2f}, law {np.round(law, 4)}")
+    assert stat < thr

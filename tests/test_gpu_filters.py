@@ -325,3 +325,38 @@ def test_gpu_stream_follows_the_filtered_target_law():
     thr = chi2_threshold(int(np.count_nonzero(law)) - 1, 1e-4)
     say(f"[filters] GPU chi-square {stat:.2f} against {thr:.2f}, law {np.round(law, 4)}")
     assert stat < thr
+
+
+def test_edge_case_rows():
+    # Rows that stress the thresholds kernel's bounds: fewer logits than threads (most threads'
+    # maxima are -inf), half the vocabulary masked to -inf, a tied maximum under top_k = 1,
+    # and extreme parameters (top_p near 0 and near 1, min_p = 1, k = V - 1).
+    from tests.helpers import batch_from_rows
+    rng = np.random.default_rng(23)
+    cases = []
+    for V in (1, 5, 300):
+        t = rng.normal(0, 2, size=(2, V)).astype(np.float32)
+        d = rng.normal(0, 2, size=(2, V)).astype(np.float32)
+        cases.append((t, d))
+    V = 4096
+    t = rng.normal(0, 3, size=(2, V)).astype(np.float32)
+    d = rng.normal(0, 3, size=(2, V)).astype(np.float32)
+    t[:, ::2] = -np.inf
+    d[:, 1::2] = -np.inf
+    cases.append((t, d))
+    t = rng.normal(0, 1, size=(2, V)).astype(np.float32)
+    t[:, 17] = t[:, 900] = t.max() + 1.0   # a tied maximum
+    cases.append((t, t.copy()))
+    params = [((1, 0.5, 0.0), (0, 0.3, 1.0)), ((4, 1e-6, 0.0), (1, 0.9999999, 0.0)),
+              ((299, 0.99, 0.5), (0, 1.0, 1.0)), ((3, 0.97, 0.0), (2000, 0.5, 1e-3)),
+              ((1, 1.0, 0.0), (1, 0.999, 0.0))]
+    for (t, d), (tp, dp) in zip(cases, params):
+        R, Vc = t.shape
+        b = batch_from_rows(t, d, [0, -1], [0, 2], [0.8], [0.0])
+        b["target_filter"] = tuple(np.array([x], dtype) for x, dtype in zip(tp, (np.int32, np.float32, np.float32)))
+        b["draft_filter"] = tuple(np.array([x], dtype) for x, dtype in zip(dp, (np.int32, np.float32, np.float32)))
+        checked, _ = check_thresholds(b, f"edge V={Vc} {tp} {dp}")
+        assert checked >= 1
+        gpu = run_gpu(b, seed=3)
+        ora = run_oracle(b, seed=3)
+        compare(b, gpu, ora)

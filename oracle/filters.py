@@ -42,11 +42,12 @@ Decisions within a band of a boundary are flagged. There the float
 arithmetic of another implementation may decide the other way:
 
 * top-p: C(v) within FILTER_EPS * S1 + TAIL_EPS * (S1 - C(theta_p)) of
-  top_p * S1, either at the crossing value or at the next larger value. The
+  top_p * S1, either at the crossing value or at the next larger value (if any). The
   second term allows for an implementation that sums the mass below the
   kept set in float32: S1 includes that mass when top-k is off, and a
   float32 exp2 term with |log2 e| <= 80 carries a relative error below 1e-5.
-* min-p: some logit with |(x - m)/T - ln(min_p)| <= MINP_EPS * max(1, |ln(min_p)|).
+* min-p: some logit with |(x - m)/T - ln(min_p)| <= MINP_EPS * max(1, |ln(min_p)|),
+  for min_p < 1 (min_p = 1 keeps exactly the logits equal to m).
 """
 from __future__ import annotations
 
@@ -116,7 +117,8 @@ def threshold(x: np.ndarray, T: float, f: Filter):
         c_at = float(cum[last])                           # C(v)
         c_above = float(cum[first - 1]) if first > 0 else 0.0  # C at the next larger value
         band = FILTER_EPS * S1 + TAIL_EPS * max(S1 - c_at, 0.0)
-        if c_at - target <= band or target - c_above <= band:
+        # At the largest value there is no larger one, so C(v) >= top_p * S1 is the only decision.
+        if c_at - target <= band or (first > 0 and target - c_above <= band):
             near = True
         theta_p = float(v)
 
@@ -127,7 +129,9 @@ def threshold(x: np.ndarray, T: float, f: Filter):
         ok = z >= lm
         theta_m = float(xs[ok].min())
         band = MINP_EPS * max(1.0, abs(lm))
-        if bool((np.abs(z[np.isfinite(z)] - lm) <= band).any()):
+        # min_p = 1: ln(1) = 0 in every implementation, and (x - m)/T = 0 exactly iff x = m,
+        # so the decision is exact.
+        if lm != 0.0 and bool((np.abs(z[np.isfinite(z)] - lm) <= band).any()):
             near = True
 
     return max(theta_k, theta_p, theta_m), near

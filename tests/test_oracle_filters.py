@@ -293,3 +293,15 @@ def test_first_token_follows_the_filtered_target_law():
     dof = int(np.count_nonzero(p_law)) - 1
     assert stat < chi2_threshold(dof, 1e-4), stat
     assert q_full.min() > 0  # the drafter's unfiltered law has full support; the filter removed some
+
+
+def test_flag_band_ignores_decisions_that_are_exact():
+    # min_p = 1 keeps exactly the maximum's ties; a crossing at the largest value has no
+    # larger value to compare with.
+    _, near = of.threshold(X5, 1.0, of.Filter(min_p=1.0))
+    assert not near
+    _, near = of.threshold(X5, 1.0, of.Filter(top_p=1e-6))
+    assert not near
+    assert kept(X5, 1.0, of.Filter(top_p=1e-6)) == {0}
+    _, near = of.threshold(X5, 1.0, of.Filter(top_p=0.5))   # the largest value's mass is top_p
+    assert near

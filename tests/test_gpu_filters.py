@@ -360,3 +360,31 @@ def test_edge_case_rows():
         gpu = run_gpu(b, seed=3)
         ora = run_oracle(b, seed=3)
         compare(b, gpu, ora)
+
+
+def test_long_windows_read_thresholds_beyond_the_first_64_rows():
+    # Requests of 80 and 70 rows, target equal to draft, so that every offered draft is accepted
+    # and the walk goes past its first 64 rows (their thresholds are read from memory, not from
+    # the lanes that prefetched the first 64), and the bonus row sits at position >= 64.
+    from tests.helpers import batch_from_rows
+    rng = np.random.default_rng(29)
+    V = 2048
+    ro = [0, 80, 150, 155]
+    R = ro[-1]
+    t = rng.normal(0, 3, size=(R, V)).astype(np.float32)
+    t[np.arange(R), rng.integers(0, V, size=R)] += 20.0   # one spike per row
+    dt = np.empty(R, dtype=np.int64)
+    for r in range(R):   # each row's draft token from its own filtered q (top-k 5, top-p 0.9)
+        q, _ = ov.row_distribution(t[r].astype(np.float64), 1.0, of.Filter(top_k=5, top_p=0.9))
+        dt[r] = rng.choice(V, p=q)
+    for hi in ro[1:]:
+        dt[hi - 1] = -1
+    b = batch_from_rows(t, t.copy(), dt, ro, [1.0, 1.0, 1.0], [0.0, 0.0, 0.0])
+    b["target_filter"] = (np.full(3, 5, np.int32), np.full(3, 0.9, np.float32), None)
+    b["draft_filter"] = (np.full(3, 5, np.int32), np.full(3, 0.9, np.float32), None)
+    for s in range(3):
+        gpu = run_gpu(b, seed=s)
+        ora = run_oracle(b, seed=s)
+        par = compare(b, gpu, ora)
+        assert par.flagged_requests == 0
+        assert list(gpu.out_accept_len) == [79, 69, 4]   # p = q: every offered draft is accepted

@@ -250,6 +250,9 @@ __device__ __forceinline__ void fold_soft(Acc& a, const CH (&x)[U], int vb, floa
   float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    // Every logit of the chunk below the threshold: nothing to add. (A filtered row with a NaN
+    // has th = +inf, so its sum stays 0 and the row fails; an unfiltered one has th = -inf.)
+    if (FILT && vm[u] < th) continue;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       float t = fast_exp2(fmaf(x[u].get(e), c, -a.mc));
@@ -1101,11 +1104,15 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     auto fold_res = [&](const CH (&xt)[U], const CH (&xd)[U], int v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (!DIAG) {  // r <= p: no token of a vector whose largest p misses pthr is a candidate
+        if (!DIAG || FILT) {
           float mt = xt[u].get(0);
 #pragma unroll
           for (int e = 1; e < VEC; ++e) mt = fmaxf(mt, xt[u].get(e));
-          if (!(fmaf(mt, c, -mct) >= sthr)) continue;
+          // r <= p: no token of a vector whose largest p misses pthr is a candidate
+          if (!DIAG && !(fmaf(mt, c, -mct) >= sthr)) continue;
+          // every target logit of the vector below the keep-threshold: p = 0, r = 0, and no
+          // token takes part in the race over p either
+          if (FILT && mt < tht) continue;
         }
         const int x0 = (v0 + u * kWave) * VEC;
         float rv[VEC], mv[VEC];

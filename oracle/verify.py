@@ -454,7 +454,7 @@ def sum_prod(p: np.ndarray, q: np.ndarray) -> float:
 
 
 def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: str,
-             tau_step=None, min_cum=None):
+             tau_step=None, min_cum=None, target_filter=None, draft_filter=None):
     """Per proposal row: sum_x min(p(x), mu(x)) and sum_x p(x) q(x).
 
     The first is the probability that the row accepts its draft given that its
@@ -467,9 +467,13 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
     A request that ``verify_request`` would fail closed on its knobs, or a row
     whose logits are invalid, gets NaN.
 
+    With ``target_filter`` / ``draft_filter`` (triples as in ``verify_batch``),
+    p and q are the filtered distributions (mlxcel PR #992, section What
+    changed), and a request whose filter values are invalid at T > 0 gets NaN.
+
     Returns (sum_min, sum_pq, near_gate): near_gate[r] marks a row with some
-    |q(x) - tau_j| < FLAG_EPS (tau_j > 0), where a float32 gate decision may
-    legitimately differ.
+    |q(x) - tau_j| < FLAG_EPS (tau_j > 0), or a filter decision in its flag
+    band, where float arithmetic may legitimately decide the other way.
     """
     target = np.asarray(target)
     R, V = target.shape
@@ -491,6 +495,9 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
         floor = 0.0 if mc is None else float(mc[b])
         if not temperature_valid(T) or np.isnan(tau[b]) or not (np.isfinite(floor) and floor >= 0.0):
             continue
+        tf, df = request_filter(target_filter, b), request_filter(draft_filter, b)
+        if T > 0.0 and any(f is not None and not filter_valid(f) for f in (tf, df)):
+            continue
         cum = 1.0
         for j in range(hi - lo - 1):
             r = lo + j
@@ -501,8 +508,8 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
             dl = decode_logits(np.asarray(draft)[r:r + 1], dtype)[0]
             if not (row_valid(tl) and row_valid(dl)):
                 break
-            p = distribution(tl, T)
-            q = distribution(dl, T)
+            p, near_p = row_distribution(tl, T, tf)
+            q, near_q = row_distribution(dl, T, df)
             tau_j = float(tau[b]) if ts is None else float(ts[r])
             if np.isnan(tau_j):
                 break
@@ -510,6 +517,6 @@ def row_sums(target, draft, draft_tokens, row_offsets, temperature, tau, dtype: 
                 tau_j = max(tau_j, floor / cum)
             smin[r] = acceptance_probability(p, retained_measure(q, tau_j))
             spq[r] = sum_prod(p, q)
-            near[r] = tau_j > 0.0 and bool((np.abs(q - tau_j) < FLAG_EPS).any())
+            near[r] = near_p or near_q or (tau_j > 0.0 and bool((np.abs(q - tau_j) < FLAG_EPS).any()))
             cum *= q[D]
     return smin, spq, near

@@ -80,3 +80,26 @@ def test_cumulative_floor_raises_later_thresholds():
     smin0, _ = _sums(t, d, [0, 0, -1], 1.0, 0.0)
     assert abs(smin0[1] - float(exact.acceptance_probability(p1, q1, F(0)))) < 1e-6
     assert smin[1] < smin0[1]
+
+
+def test_filtered_sums_match_the_exact_closed_form_on_filtered_laws():
+    # p = (1/2, 1/4, 1/8, 1/16, 1/16) under top-k 2 is (2/3, 1/3, 0, 0, 0) exactly; q under
+    # min-p 0.3 keeps the tokens with ratio >= 0.3 to its maximum. The exact closed form on
+    # those filtered laws (oracle.exact) pins the filtered sums.
+    p_law = [F(1, 2), F(1, 4), F(1, 8), F(1, 16), F(1, 16)]
+    q_law = [F(1, 10), F(4, 10), F(3, 10), F(1, 10), F(1, 10)]
+    p_f = [F(2, 3), F(1, 3), F(0), F(0), F(0)]
+    q_f = [F(0), F(4, 7), F(3, 7), F(0), F(0)]    # ratios 1/4, 1, 3/4, 1/4, 1/4: keeps 1 and 2
+    rows_t = np.stack([_logits(p_law), _logits(p_law)])
+    rows_d = np.stack([_logits(q_law), _logits(q_law)])
+    for tau in (0.0, 0.5):
+        smin, spq = _sums(rows_t, rows_d, [1, -1], 1.0, tau,
+                          target_filter=(np.array([2], np.int32), None, None),
+                          draft_filter=(None, None, np.array([0.3], np.float32)))
+        want = exact.acceptance_probability(p_f, q_f, F(tau).limit_denominator(10))
+        assert abs(smin[0] - float(want)) < 1e-6    # the logits are stored in fp32
+        assert abs(spq[0] - float(sum(a * b for a, b in zip(p_f, q_f)))) < 1e-6
+        assert np.isnan(smin[1])
+    # an invalid filter value fails the request: NaN
+    smin, _ = _sums(rows_t, rows_d, [1, -1], 1.0, 0.0, target_filter=(np.array([-1], np.int32), None, None))
+    assert np.isnan(smin[0])

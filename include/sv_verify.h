@@ -341,6 +341,27 @@ sv_status sv_verify_batch_filtered(const void* target_logits, const void* draft_
                                    size_t workspace_bytes, void* hip_stream, sv_row_diag* out_row_diag,
                                    sv_batch_stats* out_stats);
 
+/*
+ * sv_row_acceptance_filtered - sv_row_acceptance with p and q filtered.
+ *
+ * The same sums, sum_x min(p, mu) and sum_x p q per proposal row, with p and
+ * q the filtered distributions of sv_filter (mlxcel PR #992, section What
+ * changed), so that sum_x min(p, mu) is the row's acceptance probability under the
+ * sampler's own configuration. A request whose filter values are invalid at
+ * T > 0 gets NaN, as sv_verify_batch_filtered fails it. The call runs the
+ * thresholds kernel first. target_filter, draft_filter: host pointers to
+ * sv_filter, or NULL. Every other argument, the results and the errors are
+ * those of sv_row_acceptance; with both filters NULL it computes what
+ * sv_row_acceptance computes.
+ */
+sv_status sv_row_acceptance_filtered(const void* target_logits, const void* draft_logits,
+                                     const int32_t* draft_tokens, const int32_t* row_offsets,
+                                     const float* temperature, const float* tau, const float* tau_step,
+                                     const float* min_cum, const sv_filter* target_filter,
+                                     const sv_filter* draft_filter, float* out_sum_min, float* out_sum_pq,
+                                     sv_shape shape, void* workspace, size_t workspace_bytes,
+                                     void* hip_stream);
+
 /* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
 size_t sv_workspace_bytes(sv_shape shape);
 

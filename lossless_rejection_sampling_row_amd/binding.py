@@ -62,6 +62,10 @@ def load_library():
     lib.sv_row_acceptance.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
     lib.sv_row_acceptance.restype = c_int
+    lib.sv_row_acceptance_filtered.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, POINTER(SvFilter), POINTER(SvFilter), c_void_p, c_void_p,
+                                               SvShape, c_void_p, c_size_t, c_void_p]
+    lib.sv_row_acceptance_filtered.restype = c_int
     lib.sv_verify_batch_filtered.argtypes = sched[:8] + [POINTER(SvFilter), POINTER(SvFilter)] + sched[8:]
     lib.sv_verify_batch_filtered.restype = c_int
     lib.sv_filter_thresholds.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(SvFilter),
@@ -274,11 +278,13 @@ def filter_thresholds(target, draft, row_offsets, temperature, *, target_filter=
 
 
 def row_acceptance(target, draft, draft_tokens, row_offsets, temperature, tau, *, tau_step=None, min_cum=None,
-                   out_sum_min=None, out_sum_pq=None, workspace=None, stream=None):
+                   out_sum_min=None, out_sum_pq=None, workspace=None, stream=None, target_filter=None,
+                   draft_filter=None):
     """Per-row sum min(p, mu) and sum p q of a verify batch (sv_row_acceptance).
 
-    Arguments as for verify_batch. Returns (sum_min [R] float32, sum_pq [R] float32), NaN on
-    rows that are not proposal rows. Work is enqueued and not synchronised.
+    Arguments as for verify_batch; with target_filter or draft_filter the call goes to
+    sv_row_acceptance_filtered. Returns (sum_min [R] float32, sum_pq [R] float32), NaN on rows
+    that are not proposal rows. Work is enqueued and not synchronised.
     """
     import torch
     lib = load_library()
@@ -309,11 +315,16 @@ def row_acceptance(target, draft, draft_tokens, row_offsets, temperature, tau, *
         workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    _check(lib.sv_row_acceptance(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets),
-                                 _ptr(temperature), _ptr(tau), _ptr(tau_step) if tau_step is not None else None,
-                                 _ptr(min_cum) if min_cum is not None else None, _ptr(out_sum_min),
-                                 _ptr(out_sum_pq), shape, _ptr(workspace), c_size_t(workspace.numel()),
-                                 c_void_p(stream.cuda_stream)))
+    head = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets), _ptr(temperature), _ptr(tau),
+            _ptr(tau_step) if tau_step is not None else None, _ptr(min_cum) if min_cum is not None else None]
+    tail = [_ptr(out_sum_min), _ptr(out_sum_pq), shape, _ptr(workspace), c_size_t(workspace.numel()),
+            c_void_p(stream.cuda_stream)]
+    if target_filter is not None or draft_filter is not None:
+        tf = _filter_struct(target_filter, B, dev)
+        df = _filter_struct(draft_filter, B, dev)
+        _check(lib.sv_row_acceptance_filtered(*head, tf[0] if tf else None, df[0] if df else None, *tail))
+    else:
+        _check(lib.sv_row_acceptance(*head, *tail))
     return out_sum_min, out_sum_pq
 
 

@@ -1424,7 +1424,9 @@ __global__ __launch_bounds__(kBlock) void lazy_rows_kernel(Inputs in, Work w, in
 // gives row r's statistics and gate threshold, and whether every row up to r is valid. It
 // then streams its span of row r and writes one partial; merge_sums_kernel adds the w1
 // partials of each row in order. A row with an invalid row up to it gets NaN.
-template <typename E, int VEC, int U>
+// With FILT, p and q are masked by each row's keep-thresholds, and a request whose filter
+// values are invalid at T > 0 gets NaN, as the filtered verify fails it.
+template <typename E, int VEC, int U, bool FILT = false>
 __global__ __launch_bounds__(kBlock) void sums_kernel(Inputs in, Work w) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -1439,7 +1441,9 @@ __global__ __launch_bounds__(kBlock) void sums_kernel(Inputs in, Work w) {
   const int r = cls.r, b = cls.b, lo = cls.lo, j = cls.j;
   const float T = cls.T, c = fold_scale(T);
   const float floor = in.min_cum != nullptr ? in.min_cum[b] : 0.0f;
-  const bool floor_ok = __builtin_isfinite(floor) && floor >= 0.0f;
+  bool floor_ok = __builtin_isfinite(floor) && floor >= 0.0f;
+  if (FILT && T != 0.0f)
+    floor_ok = floor_ok && filter_valid(filter_params(in.filt[0], b)) && filter_valid(filter_params(in.filt[1], b));
 
   const int nw = in.w1;
   const int per = kWave / nw;  // rows per chunk
@@ -1455,9 +1459,14 @@ __global__ __launch_bounds__(kBlock) void sums_kernel(Inputs in, Work w) {
     const int Di = in.dt[rr];
     const float tsi = in.tau_step != nullptr ? in.tau_step[rr] : cls.tau;
     const int nlive = min(per, j + 1 - base);
+    float th_t = -INFINITY, th_d = -INFINITY;
+    if (FILT) {
+      th_t = in.theta[2 * (int64_t)rr];
+      th_d = in.theta[2 * (int64_t)rr + 1];
+    }
     RowStat rs;
-    const RowEval ev = eval_rows<true>(in, e, live, nw, b, min(ri, j), Di, T, tsi, floor_ok ? floor : 0.0f, carry,
-                                       nlive, c, rs);
+    const RowEval ev = eval_rows<true, FILT>(in, e, live, nw, b, min(ri, j), Di, T, tsi, floor_ok ? floor : 0.0f,
+                                             carry, nlive, c, rs, th_t, th_d);
     ok = ok && __ballot(live && ev.verdict == kRowInvalid) == 0;
     if (base + per > j) {  // the chunk that holds row r
       const int src = (j - base) * nw;
@@ -1483,6 +1492,8 @@ __global__ __launch_bounds__(kBlock) void sums_kernel(Inputs in, Work w) {
     const E* drow = reinterpret_cast<const E*>(in.draft) + (int64_t)r * in.V;
     const float mct = cur.mc_t, mcd = cur.mc_d, tau = tau_cur;
     const float ist = (float)(1.0 / cur.s_t), isd = (float)(1.0 / cur.s_d);
+    const float tht = FILT ? in.theta[2 * (int64_t)r] : -INFINITY;
+    const float thd = FILT ? in.theta[2 * (int64_t)r + 1] : -INFINITY;
     constexpr int step = U * kWave;
     float am = 0.0f, apq = 0.0f;
     CH ta[U], da[U], tb[U], db[U];
@@ -1491,8 +1502,12 @@ __global__ __launch_bounds__(kBlock) void sums_kernel(Inputs in, Work w) {
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float pp = fast_exp2(fmaf(xt[u].get(e), c, -mct)) * ist;
-          const float qq = fast_exp2(fmaf(xd[u].get(e), c, -mcd)) * isd;
+          float pp = fast_exp2(fmaf(xt[u].get(e), c, -mct)) * ist;
+          float qq = fast_exp2(fmaf(xd[u].get(e), c, -mcd)) * isd;
+          if (FILT) {
+            pp = xt[u].get(e) < tht ? 0.0f : pp;
+            qq = xd[u].get(e) < thd ? 0.0f : qq;
+          }
           am += fminf(pp, qq >= tau ? qq : 0.0f);
           apq = fmaf(pp, qq, apq);
         }
@@ -2067,10 +2082,10 @@ hipError_t launch_lazy(const Plan& p, Inputs in, const Work& w, const Outputs& o
   return hipGetLastError();
 }
 
-template <typename E, int VEC>
+template <typename E, int VEC, bool FILT = false>
 hipError_t launch_sums(const Plan& p, Inputs in, const Work& w, float* out_min, float* out_pq, hipStream_t stream) {
   constexpr int U1 = VEC == 1 ? 8 : 2;
-  const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1>);
+  const void* k1 = reinterpret_cast<const void*>(&pass1_kernel<E, VEC, U1, FILT>);
   int64_t slots1 = 0;
   hipError_t err = resident_waves(k1, kTargetWavesPerCU, &slots1);
   if (err != hipSuccess) return err;
@@ -2079,9 +2094,9 @@ hipError_t launch_sums(const Plan& p, Inputs in, const Work& w, float* out_min, 
   in.w2 = l.w2;
   const Outputs none{nullptr, nullptr, nullptr, nullptr};
   const dim3 block(kBlock);
-  hipLaunchKernelGGL((pass1_kernel<E, VEC, U1>), dim3((unsigned)l.blocks1), block, 0, stream, in, w, none);
+  hipLaunchKernelGGL((pass1_kernel<E, VEC, U1, FILT>), dim3((unsigned)l.blocks1), block, 0, stream, in, w, none);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((sums_kernel<E, VEC, U1>), dim3((unsigned)l.blocks1), block, 0, stream, in, w);
+  hipLaunchKernelGGL((sums_kernel<E, VEC, U1, FILT>), dim3((unsigned)l.blocks1), block, 0, stream, in, w);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t mb = ((int64_t)p.R + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(merge_sums_kernel, dim3((unsigned)(mb < 1024 ? mb : 1024)), block, 0, stream, in, w, out_min,
@@ -2212,12 +2227,13 @@ extern "C" sv_status sv_verify_batch_lazy(const void* target_logits, const void*
   return err == hipSuccess ? SV_OK : SV_E_HIP;
 }
 
-extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* draft_logits,
-                                       const int32_t* draft_tokens, const int32_t* row_offsets,
-                                       const float* temperature, const float* tau, const float* tau_step,
-                                       const float* min_cum, float* out_sum_min, float* out_sum_pq, sv_shape shape,
-                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
-  using namespace sv;
+namespace sv {
+
+static sv_status row_sums_run(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                              const int32_t* row_offsets, const float* temperature, const float* tau,
+                              const float* tau_step, const float* min_cum, const sv_filter* tfilt,
+                              const sv_filter* dfilt, float* out_sum_min, float* out_sum_pq, sv_shape shape,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
   Plan p;
   const sv_status st = check_call(shape, target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau,
                                   out_sum_min, out_sum_pq, workspace, workspace_bytes, &p);
@@ -2235,6 +2251,25 @@ extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* dr
                        (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;
   hipError_t err = counters_ready(p, ws, stream);
   if (err != hipSuccess) return SV_E_HIP;
+  const FilterSide ft = side_of(tfilt), fd = side_of(dfilt);
+  if (any_filter(ft) || any_filter(fd)) {
+    in.theta = reinterpret_cast<float*>(ws + p.off_theta);
+    in.filt[0] = ft;
+    in.filt[1] = fd;
+    const FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
+    if (p.dtype == SV_BF16) {
+      err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
+      if (err == hipSuccess)
+        err = aligned ? launch_sums<uint16_t, 8, true>(p, in, w, out_sum_min, out_sum_pq, stream)
+                      : launch_sums<uint16_t, 1, true>(p, in, w, out_sum_min, out_sum_pq, stream);
+    } else {
+      err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+      if (err == hipSuccess)
+        err = aligned ? launch_sums<float, 4, true>(p, in, w, out_sum_min, out_sum_pq, stream)
+                      : launch_sums<float, 1, true>(p, in, w, out_sum_min, out_sum_pq, stream);
+    }
+    return err == hipSuccess ? SV_OK : SV_E_HIP;
+  }
   if (p.dtype == SV_BF16) {
     err = aligned ? launch_sums<uint16_t, 8>(p, in, w, out_sum_min, out_sum_pq, stream)
                   : launch_sums<uint16_t, 1>(p, in, w, out_sum_min, out_sum_pq, stream);
@@ -2243,6 +2278,30 @@ extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* dr
                   : launch_sums<float, 1>(p, in, w, out_sum_min, out_sum_pq, stream);
   }
   return err == hipSuccess ? SV_OK : SV_E_HIP;
+}
+
+}  // namespace sv
+
+extern "C" sv_status sv_row_acceptance(const void* target_logits, const void* draft_logits,
+                                       const int32_t* draft_tokens, const int32_t* row_offsets,
+                                       const float* temperature, const float* tau, const float* tau_step,
+                                       const float* min_cum, float* out_sum_min, float* out_sum_pq, sv_shape shape,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return sv::row_sums_run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, tau_step,
+                          min_cum, nullptr, nullptr, out_sum_min, out_sum_pq, shape, workspace, workspace_bytes,
+                          hip_stream);
+}
+
+extern "C" sv_status sv_row_acceptance_filtered(const void* target_logits, const void* draft_logits,
+                                                const int32_t* draft_tokens, const int32_t* row_offsets,
+                                                const float* temperature, const float* tau, const float* tau_step,
+                                                const float* min_cum, const sv_filter* target_filter,
+                                                const sv_filter* draft_filter, float* out_sum_min,
+                                                float* out_sum_pq, sv_shape shape, void* workspace,
+                                                size_t workspace_bytes, void* hip_stream) {
+  return sv::row_sums_run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, tau_step,
+                          min_cum, target_filter, draft_filter, out_sum_min, out_sum_pq, shape, workspace,
+                          workspace_bytes, hip_stream);
 }
 
 extern "C" sv_status sv_verify_batch_sched(const void* target_logits, const void* draft_logits,

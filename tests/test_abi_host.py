@@ -41,6 +41,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"sv_verify_batch", "sv_verify_batch_diag", "sv_verify_batch_sched", "sv_verify_batch_lazy",
                           "sv_row_acceptance", "sv_verify_batch_filtered", "sv_filter_thresholds",
+                          "sv_row_acceptance_filtered",
                           "sv_workspace_bytes",
                           "sv_status_string", "sv_abi_version"}
     for n in names:

@@ -37,7 +37,8 @@ def _gpu_sums(batch, g=None):
     g = g or upload(batch)
     smin, spq = binding.row_acceptance(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"],
                                        g["temperature"], g["tau"], tau_step=g.get("tau_step"),
-                                       min_cum=g.get("min_cum"))
+                                       min_cum=g.get("min_cum"), target_filter=g.get("target_filter"),
+                                       draft_filter=g.get("draft_filter"))
     torch.cuda.synchronize()
     return smin.cpu().numpy().astype(np.float64), spq.cpu().numpy().astype(np.float64)
 
@@ -45,7 +46,8 @@ def _gpu_sums(batch, g=None):
 def _oracle_sums(batch):
     return ov.row_sums(batch["target"], batch["draft"], batch["draft_tokens"], batch["row_offsets"],
                        batch["temperature"], batch["tau"], batch["dtype"], tau_step=batch.get("tau_step"),
-                       min_cum=batch.get("min_cum"))
+                       min_cum=batch.get("min_cum"), target_filter=batch.get("target_filter"),
+                       draft_filter=batch.get("draft_filter"))
 
 
 def _compare(batch, label):
@@ -153,3 +155,38 @@ def test_first_row_acceptance_frequency_matches_sum_min(tau):
     say(f"[sums] first-row acceptance {freq:.4f} vs sum min {a:.4f} (sd {sd:.4f}, {tot} draws)")
     assert 0.05 < a < 0.95, "the check needs an acceptance away from 0 and 1"
     assert abs(freq - a) < 5 * sd + 1e-3
+
+
+# ---------------------------------------------------------------- under the filter chain
+
+@pytest.mark.parametrize("V,dtype", [(64, "bf16"), (4097, "f32"), (20000, "bf16")])
+def test_filtered_micro_batches(V, dtype):
+    spec = wl.Spec(B=24, T=(1, 6), V=V, dtype=dtype, sigma_t=3.0, n_spikes=min(8, V // 4), sigma_d=(0.5, 2.0),
+                   temperature=(0.5, 1.2), greedy_frac=0.1, tau=(0.0, 0.1, 0.3), noprop_frac=0.05,
+                   rng_seed=700 + V, verify_seed=1)
+    batch = as_batch(wl.generate(spec))
+    rng = np.random.default_rng(V)
+    B = len(batch["tau"])
+    for side in ("target_filter", "draft_filter"):
+        batch[side] = (rng.choice([0, 1, 5, 50, V], size=B).astype(np.int32),
+                       rng.choice([1.0, 0.5, 0.9, 0.99], size=B).astype(np.float32),
+                       rng.choice([0.0, 0.02, 0.2], size=B).astype(np.float32))
+    _compare(batch, f"filtered V={V} {dtype}")
+
+
+def test_filtered_gated_batch_full_size():
+    batch = as_batch(wl.config(3))
+    batch["target_filter"], batch["draft_filter"] = wl.sampler_filters(len(batch["tau"]), rng_seed=9)
+    _compare(batch, "filtered config 3")
+
+
+def test_invalid_filter_values_give_nan():
+    batch = as_batch(wl.generate(wl.Spec(B=6, T=3, V=512, dtype="f32", temperature=1.0, rng_seed=5, verify_seed=1)))
+    k = np.zeros(6, np.int32)
+    k[2] = -1
+    batch["target_filter"] = (k, None, None)
+    gm, _ = _gpu_sums(batch)
+    ro = batch["row_offsets"]
+    assert np.isnan(gm[ro[2]:ro[3]]).all()
+    assert np.isfinite(gm[ro[0]:ro[1] - 1]).all()
+    _compare(batch, "invalid filter")

@@ -175,3 +175,33 @@ def test_host_core_under_sanitizers():
         assert res.returncode == 0 and "OK" in res.stdout, res.stdout + res.stderr
     finally:
         shutil.rmtree(d, ignore_errors=True)
+
+
+def test_filtered_entry_points_validate_on_the_host(lib):
+    # The filtered calls check their arguments before anything is enqueued (no GPU is needed):
+    # an empty batch is SV_OK, missing pointers, a bad dtype and a short workspace are errors.
+    from lossless_rejection_sampling_row_amd.binding import SvFilter, SvShape
+    SV_OK, NULLPTR, DTYPE, WORKSPACE = 0, 1, 3, 4
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+    filt = SvFilter(None, None, None)
+    fp = ctypes.byref(filt)
+    need = lib.sv_workspace_bytes(SvShape(2, 4, 5, 1))
+
+    def thresholds(B, R, V, dt, target=fake, ws_bytes=need):
+        return lib.sv_filter_thresholds(target, fake, fake, fake, fp, fp, fake, SvShape(B, R, V, dt), fake,
+                                        ctypes.c_size_t(ws_bytes), None)
+
+    def verify(B, R, V, dt, target=fake, ws_bytes=need):
+        return lib.sv_verify_batch_filtered(target, fake, fake, fake, fake, fake, None, None, fp, None,
+                                            ctypes.c_uint64(1), fake, fake, SvShape(B, R, V, dt), fake,
+                                            ctypes.c_size_t(ws_bytes), None, None, None)
+
+    def sums(B, R, V, dt, target=fake, ws_bytes=need):
+        return lib.sv_row_acceptance_filtered(target, fake, fake, fake, fake, fake, None, None, None, fp, fake,
+                                              fake, SvShape(B, R, V, dt), fake, ctypes.c_size_t(ws_bytes), None)
+
+    for call in (thresholds, verify, sums):
+        assert call(0, 0, 5, 1) == SV_OK
+        assert call(2, 4, 5, 1, target=None) == NULLPTR
+        assert call(2, 4, 5, 7) == DTYPE
+        assert call(2, 4, 5, 1, ws_bytes=need - 1) == WORKSPACE

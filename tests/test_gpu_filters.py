@@ -105,8 +105,8 @@ def _spec(V, dtype, B=24, spikes=True, seed=0, **kw):
                    noprop_frac=0.05, rng_seed=seed, verify_seed=seed, **kw)
 
 
-@pytest.mark.parametrize("V,dtype,spikes", [(37, "f32", True), (4096, "bf16", True), (12289, "f32", False),
-                                            (32000, "bf16", True), (32000, "bf16", False)])
+@pytest.mark.parametrize("V,dtype,spikes", [(37, "f32", True), (4096, "bf16", True), (4099, "bf16", True),
+                                            (12289, "f32", False), (32000, "bf16", True), (32000, "bf16", False)])
 def test_thresholds_match_oracle(V, dtype, spikes):
     batch = as_batch(wl.generate(_spec(V, dtype, spikes=spikes, seed=300 + V)))
     rng = np.random.default_rng(V)
@@ -167,8 +167,8 @@ def _verify_parity(batch, seeds, label):
     return tot
 
 
-@pytest.mark.parametrize("V,dtype,spikes", [(64, "bf16", True), (4097, "f32", True), (16384, "bf16", False),
-                                            (40000, "bf16", True)])
+@pytest.mark.parametrize("V,dtype,spikes", [(64, "bf16", True), (4097, "f32", True), (4099, "bf16", True),
+                                            (16384, "bf16", False), (40000, "bf16", True)])
 def test_filtered_verify_matches_oracle(V, dtype, spikes):
     batch = as_batch(wl.generate(_spec(V, dtype, B=32, spikes=spikes, seed=500 + V)))
     rng = np.random.default_rng(V + 1)

@@ -159,7 +159,7 @@ def test_first_row_acceptance_frequency_matches_sum_min(tau):
 
 # ---------------------------------------------------------------- under the filter chain
 
-@pytest.mark.parametrize("V,dtype", [(64, "bf16"), (4097, "f32"), (20000, "bf16")])
+@pytest.mark.parametrize("V,dtype", [(64, "bf16"), (4097, "f32"), (4099, "bf16"), (20000, "bf16")])
 def test_filtered_micro_batches(V, dtype):
     spec = wl.Spec(B=24, T=(1, 6), V=V, dtype=dtype, sigma_t=3.0, n_spikes=min(8, V // 4), sigma_d=(0.5, 2.0),
                    temperature=(0.5, 1.2), greedy_frac=0.1, tau=(0.0, 0.1, 0.3), noprop_frac=0.05,

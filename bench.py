@@ -9,11 +9,16 @@ so that repeated steps read HBM, not the 256 MB Infinity Cache.
 It prints ONE JSON line on stdout with:
 * verified rows/s (value);
 * the whole step's algorithmic bytes per second;
-* a roofline entry for the dominant kernel (pass 1), timed with HIP events
-  recorded on the launch stream around each kernel (a second run of the same
-  steps, so that the events do not slow the timed steps);
+* a roofline entry for the dominant kernel (the one with the longer mean
+  launch, with the other beside it), timed with HIP events recorded on the
+  launch stream around each kernel (a second run of the same steps, so that
+  the events do not slow the timed steps), and its HBM traffic from the
+  counter record in profiles/ while the kernel sources match it;
 * the CPU oracle timed on a bounded sample of the same workload on this
   host's cores.
+
+--row-sums, --lazy and --filtered time the acceptance sums, the lazy verify
+and the filtered verify instead, each printing its own line.
 """
 from __future__ import annotations
 

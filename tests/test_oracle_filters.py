@@ -305,3 +305,42 @@ def test_flag_band_ignores_decisions_that_are_exact():
     assert kept(X5, 1.0, of.Filter(top_p=1e-6)) == {0}
     _, near = of.threshold(X5, 1.0, of.Filter(top_p=0.5))   # the largest value's mass is top_p
     assert near
+
+
+# ---------------------------------------------------------------- bounds the GPU kernel relies on
+
+def test_top_p_crossing_lies_inside_the_mass_window():
+    # A logit more than W = log2(V / (1 - top_p)) + 1 log2 units of mass below the maximum
+    # cannot be top-p's crossing: all such logits together hold under (1 - top_p) / 2 of the
+    # row's mass. Checked against the oracle's threshold on peaked and flat rows.
+    rng = np.random.default_rng(41)
+    for trial in range(60):
+        V = int(rng.choice([50, 1000, 20000]))
+        sigma = float(rng.choice([0.3, 1.0, 3.0, 6.0]))
+        x = rng.normal(0, sigma, size=V).astype(np.float32).astype(np.float64)
+        if trial % 3 == 0:
+            x[rng.integers(0, V, size=4)] += 8 * sigma
+        T = float(rng.choice([0.5, 1.0, 1.3]))
+        tp = float(np.float32(rng.choice([0.3, 0.9, 0.99, 0.9999])))
+        theta, _ = of.threshold(x, T, of.Filter(top_p=tp))
+        W = np.log2(V / (1.0 - tp)) + 1.0
+        depth = (x.max() - theta) / T * np.log2(np.e)   # log2 units of mass below the maximum
+        assert depth < W, (V, sigma, T, tp, depth, W)
+
+
+def test_kth_largest_block_maximum_bounds_the_kth_largest_logit():
+    # Split a row into blocks (the kernel's threads read strided blocks): at least k logits reach
+    # the k-th largest block maximum, so it is at most the row's k-th largest logit.
+    rng = np.random.default_rng(43)
+    for _ in range(200):
+        V = int(rng.integers(1, 5000))
+        nb = int(rng.choice([7, 64, 512]))
+        x = np.round(rng.normal(0, 2, size=V), 1)        # ties are common
+        k = int(rng.integers(1, min(V, nb) + 1))
+        owner = np.arange(V) % nb
+        maxima = np.full(nb, -np.inf)
+        np.maximum.at(maxima, owner, x)
+        edge = np.sort(maxima)[::-1][k - 1]
+        kth = np.sort(x)[::-1][k - 1]
+        assert edge <= kth
+        assert np.count_nonzero(x >= edge) >= k

@@ -1561,10 +1561,6 @@ __global__ __launch_bounds__(kBlock) void merge_sums_kernel(Inputs in, Work w, f
   }
 }
 
-// ====================================================================== launch
-
-// Zero the request tickets. Every ticket wraps back to zero when a call completes, so this
-// runs only when a workspace is first seen or its layout changes (see counters_ready).
 // ====================================================================== filter chain
 
 // The sampler's filter chain (mlxcel PR #992, section What changed): temperature scale,
@@ -1572,19 +1568,22 @@ __global__ __launch_bounds__(kBlock) void merge_sums_kernel(Inputs in, Work w, f
 // logit reaches a threshold, ties included, so one float per row and side describes the
 // kept set: token x is kept iff !(l_x < theta). One workgroup finds theta for one row and
 // side.
-//  - Pass A reads the row for its maximum m and validity. min-p's threshold follows from m
-//    alone: the smallest float y with (y - m) / T >= ln(min_p) in fp64.
+//  - Pass A reads the row for its maximum m and validity, and keeps per segment (the 64
+//    vectors one wave instruction reads) its largest logit and, for top-p alone, its fp32
+//    mass. min-p's threshold follows from m alone: the smallest float y with
+//    (y - m) / T >= ln(min_p) in fp64.
 //  - Pass B gathers into LDS the logits that can hold the thresholds: those at or above the
-//    k-th largest of the threads' maxima (top-k), or within W = log2(V / (1 - top_p)) + 1
-//    log2 units of mass below m (top-p alone, which holds its crossing), and sums the fp32
-//    mass of the others.
+//    k-th largest of the segments' (or threads') maxima (top-k), or within
+//    W = log2(V / (1 - top_p)) + 1 log2 units of mass below m (top-p alone, which holds its
+//    crossing), and sums the fp32 mass of the others. It re-reads only the segments whose
+//    maximum reaches that bound; the other segments' mass comes from their records.
 //  - The candidates are sorted (bitonic, in LDS). top-k's threshold is the k-th; top-p's is
 //    where the fp64 prefix mass of exp((l - m) / T) first reaches top_p times top-k's mass.
 //  - When the window holds more than kCandCap logits, or fewer than top-k's k, the filters
 //    are decided by bisection over the float order, one pass over the row per step: top-k
 //    on counts (after which top-k's set is gathered for top-p when it fits), top-p on fp64
 //    masses. Exact; the second is slow. Peaked rows keep the window small.
-constexpr int kFiltBlock = 512;  // threads per (row, side): 2 workgroups per CU fit
+constexpr int kFiltBlock = 512;  // threads per (row, side); at most 80 VGPRs: 3 workgroups per CU fit
 constexpr int kFiltWaves = kFiltBlock / kWave;
 constexpr int kCandCap = 8192;  // candidate logits one workgroup sorts in LDS
 
@@ -1596,10 +1595,17 @@ __device__ __forceinline__ int32_t order_key(float f) {
 }
 __device__ __forceinline__ float key_float(int32_t k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
 
+constexpr int kSegCap = 1024;   // segment records one workgroup keeps in LDS
+
+// A segment is the kWave vectors one wave instruction of walk_row reads: vectors
+// [kWave * s, kWave * s + kWave) of the row.
 struct FilterSmem {
   float cand[kCandCap];
+  float seg_max[kSegCap];   // each segment's largest logit
+  float seg_mass[kSegCap];  // with top-p alone: sum of exp2((l - seg_max) * c) over the segment
+  int seg_list[kSegCap];    // the segments that hold candidates
   double red[kFiltWaves];
-  int n_cand, first;
+  int n_cand, first, n_seg;
 };
 
 __device__ __forceinline__ double block_sum(double v, FilterSmem& s) {
@@ -1630,7 +1636,7 @@ __device__ __forceinline__ float block_max(float v, FilterSmem& s) {
 // cache hit, and sees ok = false), so the step function may use wave-wide operations. Loads
 // are double-buffered: the next step's vectors are in flight while step(x, ok, st) works on
 // the current ones.
-constexpr int kFiltLoads = 4;
+constexpr int kFiltLoads = 2;
 
 template <typename E, int VEC, class S>
 __device__ __forceinline__ void walk_row(const E* row, int nvec, S step) {
@@ -1705,7 +1711,7 @@ __device__ float bisect_float(float lo, float hi, P pred) {
 }
 
 template <typename E, int VEC>
-__global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, FilterArgs fa) {
+__global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6))) void thresholds_kernel(Inputs in, FilterArgs fa) {
   __shared__ FilterSmem s;
   const int r = blockIdx.x;
   const int side = blockIdx.y;
@@ -1759,12 +1765,48 @@ __global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, Filte
       }
     }
   };
-  // ---- pass A: maximum and validity
+  const float c = scale_of(T);  // log2(e) / T
+  // Segment records bound the candidates for top-k when k is at most the segment count, and
+  // for top-p alone; the gather then reads only the segments that can hold candidates.
+  const int nseg = (nvec + kWave - 1) / kWave;
+  const bool seg_k = topk && fp.k <= nseg && nseg <= kSegCap;
+  const bool seg_p = !topk && topp && nseg <= kSegCap;
+  const bool segs = seg_k || seg_p;
+  // ---- pass A: maximum and validity; each thread's largest logit; each segment's largest
+  //      logit and, with top-p alone, its mass relative to that logit
   float mx = -INFINITY;
   int bad = 0;
-  for_each_logit<E, VEC>(row, nvec, [&](float x) __attribute__((always_inline)) {
-    mx = fmaxf(mx, x);
-    bad |= (int)(__builtin_isnan(x) || x == INFINITY);
+  walk_row<E, VEC>(row, nvec, [&](const Chunk<E, VEC>(&x)[kFiltLoads], const bool (&ok)[kFiltLoads], int st)
+                                  __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kFiltLoads; ++u) {
+      float vm = -INFINITY;
+      if (ok[u]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float v = x[u].get(e);
+          vm = fmaxf(vm, v);
+          bad |= (int)(__builtin_isnan(v) || v == INFINITY);
+        }
+      }
+      mx = fmaxf(mx, vm);
+      if (segs) {
+        const int sg = (st * kFiltLoads + u) * kFiltWaves + wave;  // vectors [kWave * sg, + kWave)
+        const float sm = wave_max(vm);
+        float ms = 0.0f;
+        if (seg_p) {
+          if (ok[u] && sm > -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ms += fast_exp2((x[u].get(e) - sm) * c);
+          }
+          ms = wave_sum(ms);
+        }
+        if (lane == 0 && sg < nseg) {
+          s.seg_max[sg] = sm;
+          s.seg_mass[sg] = ms;
+        }
+      }
+    }
   });
   const float m = block_max(mx, s);
   const bool valid = block_sum((double)bad, s) == 0.0 && m != -INFINITY;
@@ -1788,19 +1830,24 @@ __global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, Filte
   }
 
   // ---- the candidates to gather
-  //  - With top-k (k <= kFiltBlock): the logits at or above the k-th largest of the threads'
-  //    maxima. At least k logits reach it, so it is at most top-k's threshold; and top-p's
-  //    crossing lies above top-k's threshold.
+  //  - With top-k: the logits at or above the k-th largest of the segments' maxima (k at
+  //    most the segment count), else of the threads' maxima (k <= kFiltBlock). Segments and
+  //    threads each split the row into disjoint parts, so at least k logits reach that
+  //    value: it is at most top-k's threshold, and top-p's crossing lies above top-k's.
   //  - With top-p alone: the logits within W = log2(V / (1 - top_p)) + 1 log2 units of mass
   //    below the maximum. A logit below that has mass under 2^-W of the maximum's, so all of
   //    them together hold less than V * 2^-W < (1 - top_p) of the row's mass (which holds
   //    the maximum): the crossing lies inside.
-  //  - With top-k beyond kFiltBlock alone: a 24-unit window, a guess checked below.
-  const float c = scale_of(T);  // log2(e) / T
+  //  - With top-k beyond both alone: a 24-unit window, a guess checked below.
   const float W = topp ? log2f((float)in.V / (1.0f - fp.top_p)) + 1.0f : 24.0f;
   float edge = -INFINITY;
-  const bool by_edge = topk && fp.k <= kFiltBlock;
-  if (by_edge) {
+  const bool by_edge = topk && (seg_k || fp.k <= kFiltBlock);
+  if (seg_k) {
+    for (int i = threadIdx.x; i < nseg; i += kFiltBlock) s.cand[i] = s.seg_max[i];
+    sort_desc(nseg);
+    edge = s.cand[fp.k - 1];
+    __syncthreads();
+  } else if (by_edge) {
     s.cand[threadIdx.x] = mx;  // -inf for a thread that read nothing
     sort_desc(kFiltBlock);
     edge = s.cand[fp.k - 1];
@@ -1848,6 +1895,64 @@ __global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, Filte
         }
       }
     });
+    rest = block_sum(tl, s);  // its barriers also publish s.n_cand and s.cand
+    return s.n_cand;
+  };
+  // gather_segments(bound, ...): the same, reading only the segments whose largest logit
+  // reaches the bound; with sum_rest the other segments' mass comes from their records. Each
+  // wave reads kFiltLoads listed segments per round trip.
+  auto gather_segments = [&](const float lo, const bool sum_rest, double& rest) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) {
+      s.n_cand = 0;
+      s.n_seg = 0;
+    }
+    __syncthreads();
+    double tl = 0.0;
+    for (int i = threadIdx.x; i < nseg; i += kFiltBlock) {
+      const float sm = s.seg_max[i];
+      if (!(sm < lo)) s.seg_list[atomicAdd(&s.n_seg, 1)] = i;
+      else if (sum_rest && sm > -INFINITY) tl += (double)s.seg_mass[i] * (double)fast_exp2((sm - m) * c);
+    }
+    __syncthreads();
+    const int ns = s.n_seg;
+    for (int i0 = wave; i0 < ns; i0 += kFiltWaves * kFiltLoads) {
+      Chunk<E, VEC> x[kFiltLoads];
+      bool ok[kFiltLoads];
+#pragma unroll
+      for (int g = 0; g < kFiltLoads; ++g) {
+        const int i = i0 + g * kFiltWaves;
+        const int v = i < ns ? s.seg_list[i] * kWave + lane : nvec;
+        ok[g] = v < nvec;
+        x[g].load(row + (int64_t)min(v, nvec - 1) * VEC);
+      }
+      int cnt = 0;
+#pragma unroll
+      for (int g = 0; g < kFiltLoads; ++g) {
+        float ts = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float v = x[g].get(e);
+          const bool cand = ok[g] && !(v < lo);
+          cnt += cand ? 1 : 0;
+          if (sum_rest && ok[g] && !cand) ts += fast_exp2((v - m) * c);
+        }
+        if (sum_rest) tl += (double)ts;
+      }
+      if (cnt > 0) {
+        int slot = atomicAdd(&s.n_cand, cnt);
+#pragma unroll
+        for (int g = 0; g < kFiltLoads; ++g) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float v = x[g].get(e);
+            if (ok[g] && !(v < lo)) {
+              if (slot < kCandCap) s.cand[slot] = v;
+              ++slot;
+            }
+          }
+        }
+      }
+    }
     rest = block_sum(tl, s);  // its barriers also publish s.n_cand and s.cand
     return s.n_cand;
   };
@@ -1906,7 +2011,7 @@ __global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, Filte
   int n = -1;           // sorted candidates in s.cand (-1: none usable)
   double rest = 0.0;    // fp32 mass of the logits outside them
   {
-    const int nw = gather(lo, topp && !topk, rest);
+    const int nw = segs ? gather_segments(lo, seg_p, rest) : gather(lo, topp && !topk, rest);
     if (nw <= kCandCap) {
       n = nw;
       sort_desc(n);
@@ -1945,6 +2050,10 @@ __global__ __launch_bounds__(kFiltBlock) void thresholds_kernel(Inputs in, Filte
   if (threadIdx.x == 0) *out = fmaxf(fmaxf(th_k, th_p), th_m);
 }
 
+// ====================================================================== launch
+
+// Zero the request tickets. Every ticket wraps back to zero when a call completes, so this
+// runs only when a workspace is first seen or its layout changes (see counters_ready).
 __global__ __launch_bounds__(kBlock) void clear_counters_kernel(uint32_t* t, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) t[i] = 0u;

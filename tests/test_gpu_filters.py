@@ -106,7 +106,8 @@ def _spec(V, dtype, B=24, spikes=True, seed=0, **kw):
 
 
 @pytest.mark.parametrize("V,dtype,spikes", [(37, "f32", True), (4096, "bf16", True), (4099, "bf16", True),
-                                            (12289, "f32", False), (32000, "bf16", True), (32000, "bf16", False)])
+                                            (12289, "f32", False), (32000, "bf16", True), (32000, "bf16", False),
+                                            (70001, "f32", True)])
 def test_thresholds_match_oracle(V, dtype, spikes):
     batch = as_batch(wl.generate(_spec(V, dtype, spikes=spikes, seed=300 + V)))
     rng = np.random.default_rng(V)

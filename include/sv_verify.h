@@ -36,7 +36,13 @@
  *    the stream has passed the call.
  *  - Host-checkable problems return a non-zero sv_status before anything is
  *    enqueued, and leave the outputs untouched.
- *  - The same inputs and seed give bit-identical outputs.
+ *  - The same inputs, seed and launch split (sv_set_tuning) give bit-identical
+ *    outputs. The split changes only the order of floating-point sums. A
+ *    different split can therefore change a request's tokens only where a
+ *    decision lies within rounding of its boundary: the accept uniform within
+ *    a relative 1e-6 of p(D)/mu(D), q(D) or some residual q_x within 1e-6 of
+ *    tau, the two best race keys within a relative 1e-6 of each other, or a
+ *    residual mass below 1e-6.
  */
 #ifndef SV_VERIFY_H
 #define SV_VERIFY_H
@@ -361,6 +367,24 @@ sv_status sv_row_acceptance_filtered(const void* target_logits, const void* draf
                                      const sv_filter* draft_filter, float* out_sum_min, float* out_sum_pq,
                                      sv_shape shape, void* workspace, size_t workspace_bytes,
                                      void* hip_stream);
+
+/*
+ * Launch tuning (host-only, process-wide). The verify calls split each
+ * potential proposal row over w1 waves and each request's last row over w2
+ * waves. A field of 0 keeps the library's choice for the device; w1 is
+ * rounded down to a power of two, and both are clamped to what the workspace
+ * holds (at most 64). Outputs depend on the split only as the determinism
+ * note at the top of this header states. It exists for measurements and for
+ * tests of that independence; normal use does not need it. It applies to
+ * calls enqueued after it returns, from any thread. sv_set_tuning(NULL)
+ * restores the defaults; sv_get_tuning reads the current values.
+ */
+typedef struct sv_tuning {
+  int32_t w1, w2;
+} sv_tuning;
+
+void sv_set_tuning(const sv_tuning* t);
+void sv_get_tuning(sv_tuning* t);
 
 /* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
 size_t sv_workspace_bytes(sv_shape shape);

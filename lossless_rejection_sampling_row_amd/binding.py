@@ -30,6 +30,11 @@ class SvShape(ctypes.Structure):
     _fields_ = [("B", c_int32), ("R", c_int32), ("V", c_int32), ("dtype", c_int32)]
 
 
+class SvTuning(ctypes.Structure):
+    """sv_tuning: launch splits (0 = the library's choice; see include/sv_verify.h)."""
+    _fields_ = [("w1", c_int32), ("w2", c_int32)]
+
+
 class SvFilter(ctypes.Structure):
     """sv_filter: one side's top_k / top_p / min_p device arrays (NULL = off)."""
     _fields_ = [("top_k", c_void_p), ("top_p", c_void_p), ("min_p", c_void_p)]
@@ -73,6 +78,10 @@ def load_library():
     lib.sv_filter_thresholds.restype = c_int
     lib.sv_verify_batch_lazy.argtypes = common + [c_int]
     lib.sv_verify_batch_lazy.restype = c_int
+    lib.sv_set_tuning.argtypes = [POINTER(SvTuning)]
+    lib.sv_set_tuning.restype = None
+    lib.sv_get_tuning.argtypes = [POINTER(SvTuning)]
+    lib.sv_get_tuning.restype = None
     lib.sv_workspace_bytes.argtypes = [SvShape]
     lib.sv_workspace_bytes.restype = c_size_t
     lib.sv_status_string.argtypes = [c_int]
@@ -108,16 +117,36 @@ def workspace_bytes(B: int, R: int, V: int, dtype_or_code) -> int:
     return int(load_library().sv_workspace_bytes(SvShape(B, R, V, code)))
 
 
+def set_tuning(**fields) -> None:
+    """Set the process-wide launch tuning (sv_set_tuning); unnamed fields are 0 (the library's
+    choice). ``set_tuning()`` restores the defaults."""
+    t = SvTuning(**{k: int(v) for k, v in fields.items()})
+    load_library().sv_set_tuning(ctypes.byref(t))
+
+
+def get_tuning() -> dict:
+    t = SvTuning()
+    load_library().sv_get_tuning(ctypes.byref(t))
+    return {name: getattr(t, name) for name, _ in SvTuning._fields_}
+
+
 _WORKSPACES: dict = {}
 
 
-def _workspace(device, nbytes: int):
-    """A zero-filled workspace per device, grown on demand. The library leaves it zeroed."""
+def _workspace(device, nbytes: int, stream):
+    """A workspace per (device, stream), grown on demand and zeroed on that stream when made.
+    Calls on different streams never share one, as the library requires of concurrent calls.
+    record_stream keeps a replaced workspace's memory from being reused before the stream's
+    work on it is done."""
     import torch
-    key = (device.type, device.index)
+    key = (device.type, device.index, int(stream.cuda_stream))
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if ws is not None:
+            ws.record_stream(stream)
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws.record_stream(stream)
         _WORKSPACES[key] = ws
     return ws
 
@@ -196,10 +225,10 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     if out_accept_len is None:
         out_accept_len = torch.empty(max(B, 0), dtype=torch.int32, device=dev)
     need = int(lib.sv_workspace_bytes(shape))
-    if workspace is None:
-        workspace = _workspace(dev, need)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, need, stream)
     args = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets), _ptr(temperature),
             _ptr(tau), c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(out_tokens),
             _ptr(out_accept_len), shape, _ptr(workspace), c_size_t(workspace.numel()),
@@ -265,10 +294,10 @@ def filter_thresholds(target, draft, row_offsets, temperature, *, target_filter=
     shape = SvShape(B, R, V, dtype_code(target.dtype))
     if out_theta is None:
         out_theta = torch.empty((R, 2), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)), stream)
     tf = _filter_struct(target_filter, B, dev)
     df = _filter_struct(draft_filter, B, dev)
     _check(lib.sv_filter_thresholds(_ptr(target), _ptr(draft), _ptr(row_offsets), _ptr(temperature),
@@ -311,10 +340,10 @@ def row_acceptance(target, draft, draft_tokens, row_offsets, temperature, tau, *
         out_sum_min = torch.empty(R, dtype=torch.float32, device=dev)
     if out_sum_pq is None:
         out_sum_pq = torch.empty(R, dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)), stream)
     head = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets), _ptr(temperature), _ptr(tau),
             _ptr(tau_step) if tau_step is not None else None, _ptr(min_cum) if min_cum is not None else None]
     tail = [_ptr(out_sum_min), _ptr(out_sum_pq), shape, _ptr(workspace), c_size_t(workspace.numel()),

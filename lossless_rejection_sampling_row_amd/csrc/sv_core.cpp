@@ -3,6 +3,8 @@
 // Pure C++ with no HIP dependency. The shared library links it, and the CPU
 // tests also build it on its own (with address and undefined-behaviour
 // sanitizers) to exercise the error paths.
+#include <mutex>
+
 #include "sv_plan.h"
 
 namespace sv {
@@ -60,17 +62,35 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   return SV_OK;
 }
 
+namespace {
+
+std::mutex g_tuning_mu;
+Tuning g_tuning{};
+
+}  // namespace
+
+Tuning tuning() {
+  std::lock_guard<std::mutex> lock(g_tuning_mu);
+  return g_tuning;
+}
+
+void set_tuning(const Tuning& t) {
+  std::lock_guard<std::mutex> lock(g_tuning_mu);
+  g_tuning = t;
+}
+
 Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2) {
   Launch l{};
+  const Tuning t = tuning();
   // Pass 1 streams the potential proposal rows: every row but the last of each request.
   // Pass 2 merges a row's partials in aligned lane groups, so the waves per row are a
   // power of two.
   const int64_t rows = p.R - p.B;
-  int64_t w1 = rows > 0 ? slots1 / rows : 1;
+  int64_t w1 = t.w1 > 0 ? t.w1 : rows > 0 ? slots1 / rows : 1;
   if (w1 > p.w1max) w1 = p.w1max;
   int64_t pow2 = 1;
   while (pow2 * 2 <= w1) pow2 *= 2;
-  int64_t w2 = p.B > 0 ? slots2 / p.B : 1;
+  const int64_t w2 = t.w2 > 0 ? t.w2 : p.B > 0 ? slots2 / p.B : 1;
   l.w1 = (int32_t)pow2;
   l.w2 = (int32_t)(w2 < 1 ? 1 : w2 > p.w2max ? p.w2max : w2);
   l.blocks1 = ceil_div(rows * l.w1, kWavesPerBlock);
@@ -116,3 +136,19 @@ extern "C" const char* sv_status_string(int status) {
 }
 
 extern "C" int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+extern "C" void sv_set_tuning(const sv_tuning* t) {
+  sv::Tuning v{};
+  if (t != nullptr) {
+    v.w1 = t->w1;
+    v.w2 = t->w2;
+  }
+  sv::set_tuning(v);
+}
+
+extern "C" void sv_get_tuning(sv_tuning* t) {
+  if (t == nullptr) return;
+  const sv::Tuning v = sv::tuning();
+  t->w1 = v.w1;
+  t->w2 = v.w2;
+}

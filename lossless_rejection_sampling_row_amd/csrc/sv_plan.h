@@ -103,7 +103,15 @@ struct Launch {
 
 // Choose the split for a device on which each kernel keeps `slots1` / `slots2` waves
 // resident: one round of waves covers the work, and no split exceeds the plan's bounds.
+// A tuning override (sv_set_tuning) replaces the computed splits, clamped to the bounds.
 Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2);
+
+// Host-side tuning (sv_set_tuning): zero fields keep the computed value.
+struct Tuning {
+  int32_t w1, w2;  // waves per potential proposal row / per request's last row
+};
+Tuning tuning();
+void set_tuning(const Tuning& t);
 
 // Validate every host-checkable argument of a verify call. The two outputs are only
 // null-checked (the acceptance sums pass their two float arrays).

@@ -18,6 +18,10 @@ gated MTP", section Approach:
 * rejection and NULL draw from the normalised (p - mu)+;
 * the last row is a bonus sample from p.
 
+The "sampler_match" rule is the comparison rule of mlxcel PR #992, section
+The premise correction: D is accepted iff it equals a fresh draw from p, and
+that draw is emitted either way.
+
 The "original" rule is that page's biased verifier from section Problem and
 result. It accepts with min(1, p/q) using the unfiltered q and draws from
 (p - q)+ on rejection. A failed gate becomes a plain sample from p.
@@ -54,6 +58,13 @@ def row_law(p, q, tau, rule="mu"):
     V = len(p)
     accepted = [Fraction(0)] * V
     fallback = [Fraction(0)] * V
+    if rule == "sampler_match":
+        # D ~ q and an independent fresh draw t ~ p; D is accepted iff D == t, and t is
+        # emitted either way (mlxcel PR #992, section The premise correction).
+        for x in range(V):
+            accepted[x] = q[x] * p[x]
+            fallback[x] = p[x] * (1 - q[x])
+        return accepted, fallback
     mu = retained_measure(q, tau)
     for D in range(V):
         if q[D] == 0:

@@ -193,6 +193,51 @@ def _top2_gap(keys: np.ndarray, cond: np.ndarray | None):
     return (k1 - k2) / k1, c
 
 
+def sampler_match_request(tl: np.ndarray, dt: np.ndarray, T: float, seed: int, b: int) -> RequestResult:
+    """The sampler-match rule (mlxcel PR #992, section The premise correction).
+
+    Every tested row takes a fresh draw t from the target p, here the row's
+    exponential race over p (the same random numbers as the method's race on
+    that row). The drafted token is accepted iff it equals t, and t is emitted
+    on both branches, so every emitted token is a draw from p. The rule reads
+    neither q nor a gate. Its acceptance is sum_x p(x) q(x) for D ~ q (the
+    same page, section The acceptance ceiling). At T = 0 the draw is the
+    lowest-index argmax. The last row, or a row with no proposal, is a bonus
+    draw as in the method.
+
+    Flags: F3 when a race's two best keys p/E lie within a relative FLAG_EPS.
+    """
+    n, V = tl.shape
+    res = RequestResult(tokens=[], accept_len=-1)
+    if not temperature_valid(T):
+        return res
+    for j in range(n):
+        if not row_valid(tl[j]):
+            res.tokens = []
+            res.rows.append(RowRecord(j=j, verdict=0))
+            return res
+        p = distribution(tl[j], T)
+        if T > 0.0:
+            E = philox.race_exponentials(seed, b, j, V)
+            t = race(p, E)
+            gap, _ = _top2_gap(p / E, None)
+            if gap < FLAG_EPS:
+                res.flags |= F_RACE
+        else:
+            t = argmax_lowest(p)
+        D = int(dt[j])
+        bonus = (j == n - 1) or not (0 <= D < V)
+        if not bonus and D == t:
+            res.rows.append(RowRecord(j=j, verdict=ACCEPT, p_D=float(p[D])))
+            res.tokens.append(D)
+            continue
+        res.rows.append(RowRecord(j=j, verdict=BONUS if bonus else REJECT))
+        res.tokens.append(t)
+        res.accept_len = len(res.tokens) - 1
+        return res
+    raise AssertionError("unreachable: the last row is always a bonus row")
+
+
 def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau: float,
                    seed: int, b: int, rule: str = "mu", tau_steps: np.ndarray | None = None,
                    min_cum: float = 0.0, tfilt: Filter | None = None,
@@ -227,6 +272,10 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
       argmax, and a rejection emits that argmax (mlxcel PR #992, section The
       acceptance ceiling).
 
+    ``rule="sampler_match"`` runs ``sampler_match_request``: a correct rule
+    with a lower acceptance, which the pages compare the method against. It
+    ignores the draft logits, tau, the schedule and the filters.
+
     Flags (method only, T > 0) mark requests whose result is decided within
     FLAG_EPS of a boundary, where float32 arithmetic may legitimately decide
     the other way:
@@ -242,6 +291,8 @@ def verify_request(tl: np.ndarray, dl: np.ndarray, dt: np.ndarray, T: float, tau
     * F5: a filter decision near its boundary on a row the method evaluates
       (``filters.threshold``).
     """
+    if rule == "sampler_match":
+        return sampler_match_request(tl, dt, T, seed, b)
     n, V = tl.shape
     res = RequestResult(tokens=[], accept_len=-1)
     if not temperature_valid(T) or np.isnan(tau) or not (np.isfinite(min_cum) and min_cum >= 0.0):

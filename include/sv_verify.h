@@ -273,6 +273,32 @@ sv_status sv_verify_batch_lazy(const void* target_logits, const void* draft_logi
                                int32_t max_rows);
 
 /*
+ * sv_verify_batch_sampler_match - the sampler-match comparison rule.
+ *
+ * mlxcel PR #992, section The premise correction: every tested row takes a
+ * fresh draw t from the target p, a drafted token is accepted iff it equals
+ * t, and t is emitted on both branches, so the emitted stream is a target
+ * sample. Its acceptance is sum_x p(x) q(x) (the same page, section The
+ * acceptance ceiling), at most the method's sum_x min(p, mu); the pages
+ * compare the method against it. It reads no draft logits and no gate.
+ * Row j of request b draws by the race over p with the random numbers of the
+ * method's race on that row (ties to the lower token id); at T_b = 0 the draw
+ * is the lowest-index argmax, which makes the rule argmax-against-argmax.
+ * The request stops at its first row whose draft differs from the draw, at
+ * a row with no proposal, or at its last row; that row's draw is its last
+ * token, and accept_len counts the rows before it.
+ * Inputs, outputs, ownership, workspace (sv_workspace_bytes of the same
+ * shape), fail-closed cases (invalid temperature, a NaN, +inf or all -inf
+ * target row up to the stop, broken row_offsets) and errors are as for
+ * sv_verify_batch. It streams every row of target_logits once.
+ */
+sv_status sv_verify_batch_sampler_match(const void* target_logits, const int32_t* draft_tokens,
+                                        const int32_t* row_offsets, const float* temperature,
+                                        uint64_t seed, int32_t* out_tokens, int32_t* out_accept_len,
+                                        sv_shape shape, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream);
+
+/*
  * sv_row_acceptance - per-row acceptance sums of a verify batch.
  *
  * For every proposal row r (row j of request b; the rows before a request's

@@ -78,6 +78,9 @@ def load_library():
     lib.sv_filter_thresholds.restype = c_int
     lib.sv_verify_batch_lazy.argtypes = common + [c_int]
     lib.sv_verify_batch_lazy.restype = c_int
+    lib.sv_verify_batch_sampler_match.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_uint64, c_void_p,
+                                                  c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
+    lib.sv_verify_batch_sampler_match.restype = c_int
     lib.sv_set_tuning.argtypes = [POINTER(SvTuning)]
     lib.sv_set_tuning.restype = None
     lib.sv_get_tuning.argtypes = [POINTER(SvTuning)]
@@ -266,6 +269,42 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
             ev = (c_void_p * 3)(*[c_void_p(int(e)) for e in events])
         _check(lib.sv_verify_batch_diag(*args, _ptr(row_diag) if row_diag is not None else None,
                                         _ptr(stats) if stats is not None else None, ev))
+    return out_tokens, out_accept_len
+
+
+def verify_sampler_match(target, draft_tokens, row_offsets, temperature, seed: int, *, out_tokens=None,
+                         out_accept_len=None, workspace=None, stream=None):
+    """The sampler-match comparison rule on the GPU (sv_verify_batch_sampler_match).
+
+    Arguments as for verify_batch, without draft logits or tau. Returns (out_tokens [R] int32,
+    out_accept_len [B] int32), enqueued and not synchronised.
+    """
+    import torch
+    lib = load_library()
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU")
+    if target.dim() != 2 or not target.is_contiguous():
+        raise ValueError("logits must be a contiguous [R, V] tensor")
+    R, V = int(target.shape[0]), int(target.shape[1])
+    B = int(row_offsets.numel()) - 1
+    for name, t, dt, n in [("draft_tokens", draft_tokens, torch.int32, R), ("row_offsets", row_offsets, torch.int32, B + 1),
+                           ("temperature", temperature, torch.float32, B)]:
+        if t.dtype != dt or t.numel() != n or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {dt} [{n}] on {dev}")
+    shape = SvShape(B, R, V, dtype_code(target.dtype))
+    if out_tokens is None:
+        out_tokens = torch.empty(R, dtype=torch.int32, device=dev)
+    if out_accept_len is None:
+        out_accept_len = torch.empty(max(B, 0), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib.sv_workspace_bytes(shape)), stream)
+    _check(lib.sv_verify_batch_sampler_match(_ptr(target), _ptr(draft_tokens), _ptr(row_offsets), _ptr(temperature),
+                                             c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(out_tokens),
+                                             _ptr(out_accept_len), shape, _ptr(workspace),
+                                             c_size_t(workspace.numel()), c_void_p(stream.cuda_stream)))
     return out_tokens, out_accept_len
 
 

@@ -2050,6 +2050,216 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   if (threadIdx.x == 0) *out = fmaxf(fmaxf(th_k, th_p), th_m);
 }
 
+// ====================================================================== sampler-match rule
+
+// The comparison rule of mlxcel PR #992, section The premise correction: every tested row
+// takes a fresh draw t from the target p, the drafted token is accepted iff it equals t,
+// and t is emitted on both branches. Its acceptance is sum_x p(x) q(x) (the same page,
+// section The acceptance ceiling). The draw on row j of request b is the race over p with
+// the same random numbers as the method's race on that row; at temperature 0 it is the
+// lowest-index argmax.
+//
+// match_rows_kernel races every row of the batch: wave gw takes span gw % nw of row
+// gw / nw and writes one MatchPart. match_emit_kernel then walks each request with one
+// wave, merging the partials of up to 64 / nw rows per round trip.
+struct MatchPart {
+  double key;    // best fp64 log key l/T - ln E of the span (T > 0)
+  int32_t idx;   // its token (-1 if none)
+  float m;       // largest logit of the span
+  int32_t bad;   // the span holds NaN or +inf
+  int32_t gidx;  // lowest index of m in the span (T = 0)
+};
+static_assert(sizeof(MatchPart) == 24, "MatchPart layout");
+
+// Request of row r: the guess for equal-length requests, else a binary search. Every read
+// stays in [0, B] whatever row_offsets holds; a broken batch is failed by the emit kernel.
+__device__ __forceinline__ int request_of_row(const Inputs& in, int r) {
+  int b = (int)((int64_t)r * in.B / in.R);
+  if (in.ro[b] <= r && r < in.ro[b + 1]) return b;
+  int lo = 0, hi = in.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (in.ro[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename E, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void match_rows_kernel(Inputs in, Work w, MatchPart* parts, int nw) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (blockIdx.x == 0) block0_duties(in, w, Outputs{nullptr, nullptr, nullptr, nullptr});
+  if (gw >= (int64_t)in.R * nw) return;
+  const int r = (int)(gw / nw), g = (int)(gw % nw);
+  const int b = uni(request_of_row(in, r));
+  const int j = r - in.ro[b];  // the row's position in its request (a counter word only)
+  const float T = in.temp[b];
+  const bool race = T != 0.0f;
+  const float c = race ? scale_of(T) : 1.0f;
+
+  using CH = Chunk<E, VEC>;
+  constexpr int step = U * kWave;
+  constexpr int G = VEC >= 4 ? 4 : 1;  // logits sharing one Philox block
+  const Span sp = wave_span(in.V / VEC, nw, g);
+  const int nsteps = (sp.end - sp.begin + step - 1) / step;
+  const E* trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
+  const uint32_t k0 = seed_lo(in.seed), k1 = seed_hi(in.seed);
+
+  Acc a = acc_empty();
+  int bad = 0;
+  Top2 t = top2_empty();
+  float wbest = -INFINITY;
+  CH ta[U], tb[U];
+  auto fold = [&](const CH (&xt)[U], int v0) __attribute__((always_inline)) {
+    if (!race) {
+      fold_max<true>(a, xt, v0, bad);
+      return;
+    }
+    fold_max<false>(a, xt, v0, bad);
+    // A log2 key l*c - log2(E) lies within (l*c - 4.06, l*c + 24), so a token more than 28.1
+    // below the wave's largest l*c cannot win (the bonus race's bound, with fp32 margins).
+    const float lb = fmaxf(wbest, wave_max(a.m) * c - 4.1f);
+    float lbest = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x0 = (v0 + u * kWave) * VEC;
+#pragma unroll
+      for (int gg = 0; gg < VEC; gg += G) {
+        float av[G];
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          av[e] = xt[u].get(gg + e) * c;
+          any |= av[e] + 25.0f >= lb;
+        }
+        if (any) {
+          const int xg = x0 + gg;
+          const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)j, (uint32_t)b, k0, k1);
+#pragma unroll
+          for (int e = 0; e < G; ++e) {
+            if (av[e] + 25.0f >= lb) {
+              const int x = xg + e;
+              const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
+              const float key = av[e] - log2_expo32(wd);
+              lbest = fmaxf(lbest, key);
+              top2_push(t, key, x, xt[u].get(gg + e), 0.0f);
+            }
+          }
+        }
+      }
+    }
+    wbest = fmaxf(wbest, wave_max(lbest));
+  };
+  if (nsteps > 0) load_chunks<true>(ta, trow, sp.begin, lane, sp.end);
+  for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+    load_chunks<true>(tb, trow, base + step, lane, sp.end);
+    mask_chunks(ta, base, lane, sp.end);
+    fold(ta, base + lane);
+    load_chunks<true>(ta, trow, base + 2 * step, lane, sp.end);
+    mask_chunks(tb, base + step, lane, sp.end);
+    fold(tb, base + step + lane);
+  }
+  float m, unused;
+  int am;
+  wave_stat(a, 0.0f, false, m, unused, am);
+  MatchPart part;
+  part.m = m;
+  part.bad = wave_or(bad);
+  part.gidx = race ? -1 : exact_argmax<CH>(trow, a, m);
+  part.key = -INFINITY;
+  part.idx = -1;
+  if (race) {
+    double bk;
+    int bi;
+    resolve_race(t, wave_max(t.k1) - kLogKeySlack,
+                 [&](int x, float l, float) {
+                   return p_logkey64((double)l, (double)T, race_word(in.seed, x, j, b));
+                 },
+                 bk, bi);
+    part.key = bk;
+    part.idx = bi == INT32_MAX ? -1 : bi;
+  }
+  if (lane == 0) parts[gw] = part;
+}
+
+// Best (key, index) within aligned groups of `width` lanes (a power of two).
+__device__ __forceinline__ void seg_best(double& k, int& i, int width) {
+  for (int o = 1; o < width; o <<= 1) {
+    const double ko = __shfl_xor(k, o);
+    const int io = __shfl_xor(i, o);
+    if (beats(ko, io, k, i)) {
+      k = ko;
+      i = io;
+    }
+  }
+}
+
+// One wave per request. Each round trip brings the partials of 64 / nw rows, lane
+// jj * nw + g holding span g of row jj; each aligned group of nw lanes merges its row.
+__global__ __launch_bounds__(kBlock) void match_emit_kernel(Inputs in, Work w, const MatchPart* parts, int nw,
+                                                             Outputs out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (gw >= in.B) return;
+  const int b = (int)gw;
+  if (!w.hdr->ro_valid) {
+    // Broken row_offsets: every output is -1. Request b clears an even share of the rows.
+    const int64_t r0 = (int64_t)b * in.R / in.B, r1 = (int64_t)(b + 1) * in.R / in.B;
+    for (int64_t r = r0 + lane; r < r1; r += kWave) out.tokens[r] = -1;
+    if (lane == 0) out.accept_len[b] = -1;
+    return;
+  }
+  const int lo = in.ro[b], hi = in.ro[b + 1];
+  const int n = hi - lo;
+  const float T = in.temp[b];
+  const int per = kWave / nw;  // rows per round trip
+  const int jj = lane / nw, g = lane % nw;
+  int stop = -1, stop_tok = -1;
+  bool invalid = !temperature_ok(T);
+  for (int base = 0; base < n && stop < 0 && !invalid; base += per) {
+    const int row = base + jj;
+    const bool live = row < n;
+    MatchPart e{-INFINITY, -1, -INFINITY, 0, -1};
+    int D = -1;
+    if (live) {
+      e = parts[(int64_t)(lo + row) * nw + g];
+      D = in.dt[lo + row];
+    }
+    float M = seg_max(e.m, nw);
+    const int bad = seg_reduce(e.bad, OpOr{}, nw);
+    double k = e.key;
+    int i = e.idx >= 0 ? e.idx : INT32_MAX;
+    seg_best(k, i, nw);
+    const int gi = seg_min(e.m == M && e.gidx >= 0 ? e.gidx : INT32_MAX, nw);
+    const int tok = T != 0.0f ? (i == INT32_MAX ? -1 : i) : (gi == INT32_MAX ? -1 : gi);
+    const bool row_bad = live && (bad != 0 || M == -INFINITY || tok < 0);
+    const bool bonus = row == n - 1 || D < 0 || D >= in.V;
+    const bool ends = live && (row_bad || bonus || D != tok);
+    // The first row of this round, in order, that ends the request.
+    const uint64_t ended = __ballot(g == 0 && ends);
+    if (ended != 0) {
+      const int first_lane = __builtin_ctzll(ended);
+      stop = base + first_lane / nw;
+      stop_tok = __shfl(tok, first_lane);
+      invalid = __shfl((int)row_bad, first_lane) != 0;
+    }
+  }
+  if (!(stop >= 0) || invalid) {
+    for (int r = lo + lane; r < hi; r += kWave) out.tokens[r] = -1;
+    if (lane == 0) out.accept_len[b] = -1;
+    return;
+  }
+  // Rows before the stop accepted their drafted tokens; the stop row emits its draw.
+  for (int r = lo + lane; r < hi; r += kWave) {
+    const int j = r - lo;
+    out.tokens[r] = j < stop ? in.dt[r] : j == stop ? stop_tok : -1;
+  }
+  if (lane == 0) out.accept_len[b] = stop;
+}
+
 // ====================================================================== launch
 
 // Zero the request tickets. Every ticket wraps back to zero when a call completes, so this
@@ -2210,6 +2420,27 @@ hipError_t launch_sums(const Plan& p, Inputs in, const Work& w, float* out_min, 
   const int64_t mb = ((int64_t)p.R + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(merge_sums_kernel, dim3((unsigned)(mb < 1024 ? mb : 1024)), block, 0, stream, in, w, out_min,
                      out_pq);
+  return hipGetLastError();
+}
+
+template <typename E, int VEC>
+hipError_t launch_match(const Plan& p, Inputs in, const Work& w, const Outputs& out, hipStream_t stream) {
+  constexpr int U = VEC == 1 ? 8 : 2;
+  const void* k = reinterpret_cast<const void*>(&match_rows_kernel<E, VEC, U>);
+  int64_t slots = 0;
+  hipError_t err = resident_waves(k, kTargetWavesPerCU2, &slots);
+  if (err != hipSuccess) return err;
+  // Waves per row: a power of two, so that the emit kernel merges rows in aligned lane groups.
+  const int64_t want = slots / (p.R > 0 ? p.R : 1);
+  int nw = 1;
+  while (nw * 2 <= want && nw * 2 <= p.w1max) nw *= 2;
+  MatchPart* parts = reinterpret_cast<MatchPart*>(reinterpret_cast<char*>(w.part1));
+  const dim3 block(kBlock);
+  const int64_t blocks1 = ((int64_t)p.R * nw + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((match_rows_kernel<E, VEC, U>), dim3((unsigned)blocks1), block, 0, stream, in, w, parts, nw);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t blocks2 = ((int64_t)p.B + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(match_emit_kernel, dim3((unsigned)blocks2), block, 0, stream, in, w, parts, nw, out);
   return hipGetLastError();
 }
 
@@ -2462,5 +2693,35 @@ extern "C" sv_status sv_filter_thresholds(const void* target_logits, const void*
     err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
   else
     err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+  return err == hipSuccess ? SV_OK : SV_E_HIP;
+}
+
+extern "C" sv_status sv_verify_batch_sampler_match(const void* target_logits, const int32_t* draft_tokens,
+                                                   const int32_t* row_offsets, const float* temperature,
+                                                   uint64_t seed, int32_t* out_tokens, int32_t* out_accept_len,
+                                                   sv_shape shape, void* workspace, size_t workspace_bytes,
+                                                   void* hip_stream) {
+  using namespace sv;
+  Plan p;
+  const sv_status st = make_plan(shape, &p);
+  if (st != SV_OK) return st;
+  if (shape.B == 0) return SV_OK;
+  if (!target_logits || !draft_tokens || !row_offsets || !temperature || !out_tokens || !out_accept_len ||
+      !workspace)
+    return SV_E_NULLPTR;
+  if (workspace_bytes < p.total) return SV_E_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  Inputs in{target_logits, nullptr, draft_tokens, row_offsets, temperature, nullptr, nullptr, nullptr,
+            seed, p.B, p.R, p.V, p.dtype, 1, 1};
+  Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
+         nullptr, nullptr, nullptr, nullptr, nullptr};
+  const Outputs out{out_tokens, out_accept_len, nullptr, nullptr};
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0;
+  hipError_t err;
+  if (p.dtype == SV_BF16)
+    err = aligned ? launch_match<uint16_t, 8>(p, in, w, out, stream) : launch_match<uint16_t, 1>(p, in, w, out, stream);
+  else
+    err = aligned ? launch_match<float, 4>(p, in, w, out, stream) : launch_match<float, 1>(p, in, w, out, stream);
   return err == hipSuccess ? SV_OK : SV_E_HIP;
 }

@@ -412,6 +412,32 @@ typedef struct sv_tuning {
 void sv_set_tuning(const sv_tuning* t);
 void sv_get_tuning(sv_tuning* t);
 
+/*
+ * sv_verify_batch_static - sv_verify_batch without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc.
+ *
+ * Inputs, outputs, results and errors are those of sv_verify_batch (the same
+ * kernels run). The workspace is a device array of SV_STATIC_WORKSPACE_BYTES
+ * inside the library, one per GPU, held until the process ends. Its address
+ * is looked up on the first call on each device. A shape whose
+ * sv_workspace_bytes exceeds SV_STATIC_WORKSPACE_BYTES returns
+ * SV_E_WORKSPACE before anything is enqueued. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (on different streams, or
+ * from several threads without ordering) race and give undefined outputs.
+ * Calls in one stream are ordered and safe. The first call on a device, and
+ * a call whose shape changes the workspace layout, enqueue a small kernel
+ * that zeroes the array's counters.
+ */
+#define SV_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+
+sv_status sv_verify_batch_static(const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_tokens, const int32_t* row_offsets,
+                                 const float* temperature, const float* tau, uint64_t seed,
+                                 int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
+                                 void* hip_stream);
+
 /* Bytes of workspace the call needs for this shape; 0 when the shape is invalid. Host-only. */
 size_t sv_workspace_bytes(sv_shape shape);
 

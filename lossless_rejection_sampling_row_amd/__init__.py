@@ -7,7 +7,7 @@ ABI. Names are resolved lazily, so importing the package (for example to use
 """
 _BINDING_NAMES = {
     "ABI_VERSION", "SvError", "library_path", "load_library", "verify_batch", "workspace_bytes",
-    "verify_sampler_match", "filter_thresholds", "row_acceptance", "expand_schedule", "split_row_diag", "set_tuning", "get_tuning",
+    "verify_sampler_match", "verify_batch_static", "filter_thresholds", "row_acceptance", "expand_schedule", "split_row_diag", "set_tuning", "get_tuning",
 }
 
 

@@ -78,6 +78,8 @@ def load_library():
     lib.sv_filter_thresholds.restype = c_int
     lib.sv_verify_batch_lazy.argtypes = common + [c_int]
     lib.sv_verify_batch_lazy.restype = c_int
+    lib.sv_verify_batch_static.argtypes = common[:10] + [c_void_p]
+    lib.sv_verify_batch_static.restype = c_int
     lib.sv_verify_batch_sampler_match.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_uint64, c_void_p,
                                                   c_void_p, SvShape, c_void_p, c_size_t, c_void_p]
     lib.sv_verify_batch_sampler_match.restype = c_int
@@ -269,6 +271,29 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
             ev = (c_void_p * 3)(*[c_void_p(int(e)) for e in events])
         _check(lib.sv_verify_batch_diag(*args, _ptr(row_diag) if row_diag is not None else None,
                                         _ptr(stats) if stats is not None else None, ev))
+    return out_tokens, out_accept_len
+
+
+STATIC_WORKSPACE_BYTES = 16 << 20  # SV_STATIC_WORKSPACE_BYTES
+
+
+def verify_batch_static(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int, out_tokens,
+                        out_accept_len, *, stream=None):
+    """sv_verify_batch_static: verify_batch with the library's own per-GPU workspace. The caller
+    passes the outputs ([R] and [B] int32 tensors); the call allocates nothing."""
+    import torch
+    lib = load_library()
+    R, V = int(target.shape[0]), int(target.shape[1])
+    B = int(row_offsets.numel()) - 1
+    if out_tokens.dtype != torch.int32 or out_tokens.numel() != R or out_accept_len.dtype != torch.int32 \
+            or out_accept_len.numel() != B:
+        raise ValueError("out_tokens must be int32 [R] and out_accept_len int32 [B]")
+    if stream is None:
+        stream = torch.cuda.current_stream(target.device)
+    shape = SvShape(B, R, V, dtype_code(target.dtype))
+    _check(lib.sv_verify_batch_static(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(row_offsets),
+                                      _ptr(temperature), _ptr(tau), c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                      _ptr(out_tokens), _ptr(out_accept_len), shape, c_void_p(stream.cuda_stream)))
     return out_tokens, out_accept_len
 
 

@@ -2507,6 +2507,40 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
   return err == hipSuccess ? SV_OK : SV_E_HIP;
 }
 
+// The allocation-free verify's workspace: one array per GPU in the code object, so no call
+// allocates. Host code never passes `scratch` itself to a kernel (on the host it only names
+// the symbol); it uses the device address that hipGetSymbolAddress returns for the current
+// device, kept per device.
+static __device__ __align__(256) unsigned char scratch[SV_STATIC_WORKSPACE_BYTES];
+
+struct ScratchSeen {
+  int device;
+  void* ptr;
+};
+
+static std::mutex g_scratch_mu;
+static ScratchSeen g_scratch[64];
+static int g_scratch_n = 0;
+
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (int i = 0; i < g_scratch_n; ++i)
+    if (g_scratch[i].device == dev) {
+      *out = g_scratch[i].ptr;
+      return hipSuccess;
+    }
+  if (g_scratch_n >= 64) return hipErrorInvalidDevice;
+  void* ptr = nullptr;
+  if ((err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return err;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  g_scratch[g_scratch_n++] = ScratchSeen{dev, ptr};
+  *out = ptr;
+  return hipSuccess;
+}
+
 }  // namespace sv
 
 extern "C" sv_status sv_verify_batch(const void* target_logits, const void* draft_logits,
@@ -2724,4 +2758,24 @@ extern "C" sv_status sv_verify_batch_sampler_match(const void* target_logits, co
   else
     err = aligned ? launch_match<float, 4>(p, in, w, out, stream) : launch_match<float, 1>(p, in, w, out, stream);
   return err == hipSuccess ? SV_OK : SV_E_HIP;
+}
+
+extern "C" sv_status sv_verify_batch_static(const void* target_logits, const void* draft_logits,
+                                            const int32_t* draft_tokens, const int32_t* row_offsets,
+                                            const float* temperature, const float* tau, uint64_t seed,
+                                            int32_t* out_tokens, int32_t* out_accept_len, sv_shape shape,
+                                            void* hip_stream) {
+  sv::Plan p;
+  const sv_status st = sv::make_plan(shape, &p);
+  if (st != SV_OK) return st;
+  if (shape.B == 0) return SV_OK;
+  if (!target_logits || !draft_logits || !draft_tokens || !row_offsets || !temperature || !tau || !out_tokens ||
+      !out_accept_len)
+    return SV_E_NULLPTR;
+  if (p.total > SV_STATIC_WORKSPACE_BYTES) return SV_E_WORKSPACE;
+  void* ws = nullptr;
+  if (sv::scratch_address(&ws) != hipSuccess) return SV_E_HIP;
+  return sv::run(target_logits, draft_logits, draft_tokens, row_offsets, temperature, tau, nullptr, nullptr,
+                 seed, out_tokens, out_accept_len, shape, ws, SV_STATIC_WORKSPACE_BYTES, hip_stream,
+                 nullptr, nullptr, nullptr);
 }

@@ -205,3 +205,29 @@ def test_filtered_entry_points_validate_on_the_host(lib):
         assert call(2, 4, 5, 1, target=None) == NULLPTR
         assert call(2, 4, 5, 7) == DTYPE
         assert call(2, 4, 5, 1, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_static_entry_point_validates_on_the_host(lib):
+    # The allocation-free verify checks its arguments, and that the shape's workspace fits its
+    # per-GPU array, before it looks up the array or enqueues anything.
+    from lossless_rejection_sampling_row_amd.binding import STATIC_WORKSPACE_BYTES, SvShape
+    SV_OK, NULLPTR, SHAPE, DTYPE, WORKSPACE = 0, 1, 2, 3, 4
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+
+    def call(B, R, V, dt, null=None):
+        ptrs = [fake] * 8
+        if null is not None:
+            ptrs[null] = None
+        return lib.sv_verify_batch_static(*ptrs[:6], ctypes.c_uint64(1), *ptrs[6:], SvShape(B, R, V, dt), None)
+
+    m = re.search(r"#define SV_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == STATIC_WORKSPACE_BYTES
+    assert call(0, 0, 5, 1) == SV_OK
+    assert call(2, 1, 5, 1) == SHAPE
+    assert call(2, 4, 5, 9) == DTYPE
+    for i in range(8):
+        assert call(2, 4, 5, 1, null=i) == NULLPTR
+    big = SvShape(1024, 9216, 262144, 0)
+    assert lib.sv_workspace_bytes(big) > STATIC_WORKSPACE_BYTES
+    assert call(1024, 9216, 262144, 0) == WORKSPACE
+    assert lib.sv_workspace_bytes(SvShape(512, 2560, 152064, 0)) <= STATIC_WORKSPACE_BYTES  # 512 x 5 x 152064 fits

@@ -1,0 +1,76 @@
+"""The flag rate at scale, and parity on every request it covers.
+
+A flagged request has a decision within 1e-6 of its boundary (the oracle's F1-F4), so
+float32 may take it the other way; parity tests leave it out and count it. Here the count
+is taken over the benchmark batches: the ungated B=32, T=4, V=128256 and gated B=64, T=4,
+V=151936 bf16 batches in full over 100 seeds each, and 1024 requests each of the ungated
+B=256, T=8, V=256000 and mixed-policy B=512, T=4, V=152064 batches. Summed over all of
+them, flagged requests must number fewer than 1e-4 of the rows. Every other request must
+match the oracle bit for bit. The oracle runs in a host process pool while the GPU works.
+"""
+import numpy as np
+import pytest
+
+from lossless_rejection_sampling_row_amd import workloads as wl
+from tests import oracle_pool
+from tests.gpu_util import as_batch, run_gpu, say, upload
+
+pytestmark = pytest.mark.gpu
+
+# (configuration, seeds, requests per oracle task)
+PLAN = [(2, range(100), None), (3, range(100), None), (4, range(4), 32), (5, range(2), 64)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_rejection_sampling_row_amd import binding
+    binding.load_library()
+    yield
+
+
+def test_flag_rate_and_parity_at_scale():
+    n = oracle_pool.workers()
+    say(f"[flag-rate] oracle pool of {n} workers")
+    with oracle_pool.make_pool(n) as pool:
+        futures = {}
+        for cfg, seeds, chunk in PLAN:
+            B = wl.CONFIGS[cfg].B
+            for s in seeds:
+                reqs = list(range(B))
+                parts = [reqs] if chunk is None else [reqs[i:i + chunk] for i in range(0, B, chunk)]
+                for part in parts:
+                    futures[(cfg, s, part[0])] = (part, pool.submit(oracle_pool.oracle_task, cfg, s, part))
+        total_rows = total_flagged = 0
+        for cfg, seeds, chunk in PLAN:
+            batch = as_batch(wl.config(cfg))
+            g = upload(batch)
+            ro = np.asarray(batch["row_offsets"], dtype=np.int64)
+            rows = flagged = flagged_rows = 0
+            for s in seeds:
+                gpu = run_gpu(batch, seed=s, gpu=g, diag=False)
+                for (c, ss, _), (part, fut) in futures.items():
+                    if c != cfg or ss != s:
+                        continue
+                    flags, lens, toks = fut.result()
+                    for b in part:
+                        lo, hi = int(ro[b]), int(ro[b + 1])
+                        rows += hi - lo
+                        if flags[b]:
+                            flagged += 1
+                            flagged_rows += hi - lo
+                            say(f"[flag-rate] {wl.CONFIG_NAMES[cfg]} seed={s} request {b} flags={int(flags[b])}")
+                            continue
+                        assert gpu.out_accept_len[b] == lens[b], (cfg, s, b, gpu.out_accept_len[b], lens[b])
+                        assert np.array_equal(gpu.out_tokens[lo:hi], toks[lo:hi]), (cfg, s, b)
+            say(f"[flag-rate] {wl.CONFIG_NAMES[cfg]}: {len(seeds)} seeds, {rows} rows, "
+                f"{flagged} flagged requests ({flagged_rows} rows), rate {flagged / rows:.2e} per row")
+            total_rows += rows
+            total_flagged += flagged
+            del g
+    say(f"[flag-rate] all: {total_rows} rows, {total_flagged} flagged requests, "
+        f"rate {total_flagged / total_rows:.2e} per row")
+    assert total_rows >= 60000
+    assert total_flagged < 1e-4 * total_rows

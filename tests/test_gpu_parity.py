@@ -9,7 +9,8 @@ The bar:
 * the residual mass agrees to max(1e-5 * R, 2e-6).
 
 Flagged requests have a decision within 1e-6 of a boundary, so fp32 may
-decide them the other way. They are counted and must stay below 1e-4 of rows.
+decide them the other way. They are counted here; their rate over the
+benchmark batches at scale is the subject of test_gpu_flag_rate.py.
 """
 import numpy as np
 import pytest
@@ -258,12 +259,3 @@ def test_chi_square_on_gpu(stat_samples):
         toks = emitted_tokens(gpu.out_tokens, gpu.out_accept_len, batch["row_offsets"])[:stat_samples]
         assert toks.size == stat_samples
         assert chi_square(toks, p) < chi2_threshold(5, 1e-4)
-
-
-def test_flag_rate_over_many_seeds():
-    tot = Parity()
-    for cfg, seeds in ((2, range(3, 23)), (3, range(4, 84))):
-        batch = as_batch(wl.config(cfg))
-        tot.add(_parity(batch, seeds=seeds, label=f"flag-rate {wl.CONFIG_NAMES[cfg]}"))
-    say(f"[flag-rate] {tot}")
-    assert tot.flagged_rows < 1e-4 * tot.rows + 1e-9 or tot.flagged_requests <= 1

@@ -112,23 +112,92 @@ def tested_rows(w, accept_len: np.ndarray) -> int:
     return n
 
 
-def cpu_baseline(w, budget_s: float):
-    """Time the oracle as it stands on one process over whole batches of this workload."""
+POOL_CAP = 16  # a one-GPU machine's share of host cores, whatever the affinity mask shows
+_POOL_W = None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _pool_init(cfg: int) -> None:
+    global _POOL_W
+    from lossless_rejection_sampling_row_amd import workloads as wl
+    _POOL_W = wl.config(cfg)
+
+
+def _pool_ready(_: int) -> int:
+    time.sleep(0.2)  # keep this worker busy so that every worker takes one
+    return os.getpid()
+
+
+def _pool_task(seed: int, b0: int, b1: int) -> int:
+    """The oracle on requests b0 .. b1-1 of the worker's batch; returns the rows it verified."""
     from oracle import verify as ov
-    rows = 0
-    calls = 0
+    w = _POOL_W
+    ov.verify_batch(w.target, w.draft, w.draft_tokens, w.row_offsets, w.temperature, w.tau, seed, w.dtype,
+                    requests=range(b0, b1))
+    return int(w.row_offsets[b1] - w.row_offsets[b0])
+
+
+def _single_leg(w, budget_s: float):
+    from oracle import verify as ov
+    rows = calls = 0
     t0 = time.perf_counter()
     while True:
-        ov.verify_batch(w.target, w.draft, w.draft_tokens, w.row_offsets, w.temperature, w.tau,
-                        calls, w.dtype)
+        ov.verify_batch(w.target, w.draft, w.draft_tokens, w.row_offsets, w.temperature, w.tau, calls, w.dtype)
         rows += w.R
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} full batches of the same workload (seeds 0..{calls - 1}), "
-                      f"{rows} rows in {el:.1f} s, one process (numpy, single-threaded)"}
+    return {"value": rows / el, "unit": "rows/s", "cores": 1,
+            "sample": f"{calls} full batches (seeds 0..{calls - 1}), {rows} rows in {el:.1f} s, one process"}
+
+
+def _pool_leg(cfg: int, w, budget_s: float):
+    import multiprocessing as mp
+    from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
+    avail = len(os.sched_getaffinity(0))
+    n = max(1, min(avail, POOL_CAP))
+    chunk = max(1, min(4, w.B))
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"), initializer=_pool_init,
+                             initargs=(cfg,)) as pool:
+        for f in [pool.submit(_pool_ready, i) for i in range(n)]:
+            f.result()  # every worker has built the batch before the clock starts
+        jobs = ((seed, b, min(b + chunk, w.B)) for seed in range(1 << 30) for b in range(0, w.B, chunk))
+        rows = tasks = 0
+        t0 = time.perf_counter()
+        live = {pool.submit(_pool_task, *next(jobs)) for _ in range(2 * n)}
+        while live:
+            done, live = wait(live, return_when=FIRST_COMPLETED)
+            for f in done:
+                rows += f.result()
+                tasks += 1
+            if time.perf_counter() - t0 < budget_s:
+                live |= {pool.submit(_pool_task, *next(jobs)) for _ in done}
+        el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "rows/s", "cores": n,
+            "sample": f"{tasks} tasks of {chunk} requests over seeds 0.., {rows} rows in {el:.1f} s, "
+                      f"a pool of {n} processes ({avail} cores in the affinity mask, at most {POOL_CAP} used)"}
+
+
+def cpu_baseline(cfg: int, w, budget_s: float):
+    """Time the oracle as it stands on this host: one process over whole batches of the workload,
+    then a spawn pool of processes over its requests on the cores this process may use."""
+    one = _single_leg(w, budget_s / 2)
+    many = _pool_leg(cfg, w, budget_s / 2)
+    model = cpu_model()
+    return {"value": many["value"], "unit": "rows/s", "cores": many["cores"], "kind": "oracle",
+            "sample": many["sample"], "cpu_model": model,
+            "legs": [dict(one, cpu_model=model), dict(many, cpu_model=model)]}
 
 
 def _counter_means(path, counter):
@@ -409,7 +478,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--sets", type=int, default=None, help="distinct input sets rotated through")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle timing, split between the one-process and pool legs (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the steps, copy a MIB-MiB device buffer three times (a plain copy of known size "
                          "whose FETCH_SIZE / WRITE_SIZE scale the counters of the verify kernels)")
@@ -568,7 +638,7 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(w0, args.cpu_budget)
+        cpu = cpu_baseline(args.config, w0, args.cpu_budget)
 
     line = {
         "metric": METRIC,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 
 typedef enum sv_status {
   SV_OK = 0,
@@ -111,6 +111,12 @@ typedef struct sv_batch_stats {
   int64_t bonus;        /* requests that ended with a bonus draw              */
   int64_t greedy;       /* valid requests at temperature 0                    */
   int64_t invalid;      /* requests failed closed on the device               */
+  int64_t offered;      /* proposal rows whose draft passed the gate and was
+                           tested (accepted + rejected)                     */
+  int64_t noprop;       /* requests that stopped at a row with no proposal
+                           before their last row                            */
+  int64_t bad_draft;    /* ... of them, those whose drafted id was neither -1
+                           nor in [0, V) (read as no proposal)              */
 } sv_batch_stats;
 
 /*

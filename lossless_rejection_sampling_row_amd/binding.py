@@ -11,7 +11,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_int, c_int32, c_size_t, c_uint64, c_void_p
 
-ABI_VERSION = 1
+ABI_VERSION = 2
+# sv_batch_stats, in order: requests, rows_tested, accepted, rejected, null_rows, bonus, greedy,
+# invalid, offered, noprop, bad_draft.
+STATS_FIELDS = 11
 SV_F32, SV_BF16 = 0, 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -186,7 +189,7 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     tau           : [B] float32 gate thresholds.
     seed          : 64-bit Philox key.
     row_diag      : optional [R, 8] int32 tensor that receives sv_row_diag records.
-    stats         : optional [8] int64 tensor that receives sv_batch_stats.
+    stats         : optional [STATS_FIELDS] int64 tensor that receives sv_batch_stats.
     events        : optional sequence of three raw hipEvent_t handles (ints).
     tau_step      : optional [R] float32 per-row gate thresholds (see expand_schedule).
     min_cum       : optional [B] float32 cumulative floors (0 = off).
@@ -240,8 +243,8 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
             c_void_p(stream.cuda_stream)]
     if row_diag is not None and (row_diag.dtype != torch.int32 or row_diag.numel() != 8 * R):
         raise ValueError("row_diag must be an int32 tensor with 8*R elements")
-    if stats is not None and (stats.dtype != torch.int64 or stats.numel() != 8):
-        raise ValueError("stats must be an int64 tensor with 8 elements")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() != STATS_FIELDS):
+        raise ValueError(f"stats must be an int64 tensor with {STATS_FIELDS} elements")
     if target_filter is not None or draft_filter is not None:
         if events is not None or lazy_max_rows is not None:
             raise ValueError("the filtered verify takes no events and has no lazy form")

@@ -371,7 +371,8 @@ __device__ void block0_duties(const Inputs& in, const Work& w, const Outputs& ou
   if (bad) atomicOr(&s_bad, 1);
   __syncthreads();
   if (threadIdx.x == 0) w.hdr->ro_valid = s_bad ? 0 : 1;
-  if (out.stats != nullptr && threadIdx.x < 8) reinterpret_cast<int64_t*>(out.stats)[threadIdx.x] = 0;
+  constexpr int kStats = (int)(sizeof(sv_batch_stats) / sizeof(int64_t));
+  if (out.stats != nullptr && threadIdx.x < kStats) reinterpret_cast<int64_t*>(out.stats)[threadIdx.x] = 0;
 }
 
 
@@ -842,7 +843,9 @@ __device__ __forceinline__ ReqState walk_request(const Inputs& in, const Work& w
   return q;
 }
 
-__device__ __forceinline__ void add_stats(const Outputs& out, const ReqState& q, bool invalid) {
+// One lane per request adds its counts (sv_batch_stats field order). D is the drafted id on
+// the request's last evaluated row.
+__device__ __forceinline__ void add_stats(const Outputs& out, const ReqState& q, bool invalid, int D, int V) {
   if (out.stats == nullptr) return;
   unsigned long long* s = reinterpret_cast<unsigned long long*>(out.stats);
   if (invalid) {
@@ -857,6 +860,12 @@ __device__ __forceinline__ void add_stats(const Outputs& out, const ReqState& q,
   if (q.final_verdict == SV_ROW_NULL) atomicAdd(s + 4, 1ull);
   if (q.final_verdict == SV_ROW_BONUS) atomicAdd(s + 5, 1ull);
   if (q.T == 0.0f) atomicAdd(s + 6, 1ull);
+  const int offered = q.k + (q.final_verdict == SV_ROW_REJECT ? 1 : 0);
+  if (offered) atomicAdd(s + 8, (unsigned long long)offered);
+  if (q.final_verdict == SV_ROW_BONUS && q.k < q.n - 1) {
+    atomicAdd(s + 9, 1ull);
+    if (D != SV_NO_PROPOSAL && (D < 0 || D >= V)) atomicAdd(s + 10, 1ull);
+  }
 }
 
 // Write request b's outputs (one wave): the accepted drafts, the last token, -1 after it.
@@ -870,7 +879,7 @@ __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, co
   }
   if (lane == 0) {
     out.accept_len[b] = invalid ? -1 : q.k;
-    add_stats(out, q, invalid);
+    add_stats(out, q, invalid, (!invalid && q.k < q.n) ? in.dt[q.lo + q.k] : SV_NO_PROPOSAL, in.V);
   }
   if (out.diag != nullptr) {
     if (invalid) {

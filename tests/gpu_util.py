@@ -74,7 +74,7 @@ def run_gpu(batch, seed=None, gpu=None, diag=True):
     g = gpu if gpu is not None else upload(batch)
     R = int(g["target"].shape[0])
     row_diag = torch.full((R, 8), -7, dtype=torch.int32, device="cuda") if diag else None
-    stats = torch.full((8,), -7, dtype=torch.int64, device="cuda") if diag else None
+    stats = torch.full((binding.STATS_FIELDS,), -7, dtype=torch.int64, device="cuda") if diag else None
     toks, lens = binding.verify_batch(g["target"], g["draft"], g["draft_tokens"], g["row_offsets"],
                                       g["temperature"], g["tau"], batch["seed"] if seed is None else seed,
                                       row_diag=row_diag, stats=stats, tau_step=g.get("tau_step"),

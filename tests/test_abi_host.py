@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
                           "sv_status_string", "sv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.sv_abi_version() == 1
+    assert lib.sv_abi_version() == 2
 
 
 def _call(lib, B, R, V, dtype, ws_bytes=1 << 30, null=None, diag=False):

@@ -116,6 +116,23 @@ def test_stats_counters():
     assert gpu.stats[1] == k[valid].sum() + gpu.stats[3] + gpu.stats[4]
     assert gpu.stats[6] == ((batch["temperature"] == 0) & valid).sum()
     assert gpu.stats[7] == (~valid).sum()
+    assert gpu.stats[8] == k[valid].sum() + gpu.stats[3]            # offered = accepted + rejected
+    last = ro[1:][valid] - 1
+    noprop = (v[final] == 4) & (final < last)
+    assert gpu.stats[9] == noprop.sum() and gpu.stats[9] > 0
+    assert gpu.stats[10] == 0
+    # Drafted ids outside [0, V) other than -1 read as no proposal, and are counted as bad.
+    V = batch["target"].shape[1]
+    bad = dict(batch)
+    bad["draft_tokens"] = np.array(batch["draft_tokens"], copy=True)
+    holes = np.flatnonzero(bad["draft_tokens"] == -1)
+    bad["draft_tokens"][holes[0::3]] = V + 3
+    bad["draft_tokens"][holes[1::3]] = -9
+    g2 = run_gpu(bad, seed=3)
+    assert np.array_equal(g2.out_tokens, gpu.out_tokens) and np.array_equal(g2.out_accept_len, k)
+    assert np.array_equal(g2.stats[:10], gpu.stats[:10])
+    dfin = bad["draft_tokens"][final]
+    assert g2.stats[10] == (noprop & (dfin != -1)).sum() and g2.stats[10] > 0
 
 
 # ---------------------------------------------------------------- edge cases

@@ -55,6 +55,8 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   // sums' per-row done flags.
   q.off_ticket2 = off = align_up(off, 256);
   off += (size_t)q.B * sizeof(uint32_t);
+  q.off_bmax = off = align_up(off, 8);  // the bonus race's per-request best (logit, token)
+  off += (size_t)q.B * sizeof(uint64_t);
   q.off_done3 = off;
   off += (size_t)q.R * sizeof(uint32_t);
   q.total = align_up(off, 256);

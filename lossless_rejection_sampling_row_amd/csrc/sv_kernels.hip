@@ -103,6 +103,9 @@ struct Work {
   SumPart* part3;   // acceptance sums: one partial per (row, wave)
   uint32_t* done3;  // acceptance sums: rows that hold partials (reset by the merge)
   int32_t* lazy_stop;  // lazy verify: the request's window has stopped
+  // Bonus races: per request, the largest (logit, token) any of its waves has seen, packed by
+  // pack_best. Zero between calls: the request's merging wave clears it.
+  uint64_t* bmax = nullptr;
 };
 
 struct Outputs {
@@ -923,6 +926,38 @@ __device__ __forceinline__ double p_logkey64(double l, double T, uint32_t word) 
   return l / T - log(expo64(word));
 }
 
+// Race candidate queue of a pass-2 instance: a fold pushes at most U * VEC / G groups per
+// lane (G tokens share a Philox block), on top of the fewer than 64 that a drain leaves.
+template <int VEC, int U>
+constexpr int queue_cap() {
+  return (U * VEC / (VEC >= 4 ? 4 : 1) + 1) * kWave;
+}
+
+// A (logit, token) pair as one 64-bit word whose unsigned order is the logit's order: the
+// float's bits mapped to a monotone unsigned key in the high half, the token in the low half.
+// Zero is below every pair.
+__device__ __forceinline__ uint64_t pack_best(float l, int x) {
+  const uint32_t u = __float_as_uint(l);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)k << 32) | (uint32_t)x;
+}
+
+__device__ __forceinline__ float best_logit(uint64_t v) {
+  const uint32_t k = (uint32_t)(v >> 32);
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // The race winner among the lanes' fp32 top-2 candidates. Every candidate whose fp32 key
 // reaches `cut` is re-evaluated exactly by `eval(index, a, b)`; the best exact key wins,
 // ties to the lower index. With `cut` a safe margin below the wave's best fp32 key, no
@@ -977,6 +1012,12 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  // Each wave's queue of race candidate groups (see the draw loops).
+  constexpr int kQueueCap = queue_cap<VEC, U>();
+  __shared__ int q_x[kWavesPerBlock][kQueueCap];
+  constexpr int kQG = VEC >= 4 ? 4 : 1;  // tokens per queued group
+  __shared__ float q_t[kWavesPerBlock][kQueueCap * kQG];
+  __shared__ float q_d[kWavesPerBlock][kQueueCap * kQG];
   if (gw >= (int64_t)in.B * in.w2) return;
   const int b = (int)(gw / in.w2);
   const int g = (int)(gw % in.w2);
@@ -1110,18 +1151,49 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     const bool prace = FILT && tht > -INFINITY;
     const float plb = q.stop.m_t * c - 29.0f;
     Top2 tq = top2_empty();
+    // Candidate groups (G tokens that share a Philox block) wait in the wave's queue and are
+    // drawn 64 at a time, one group per lane: a Philox block costs a wave the same whether
+    // one lane needs it or all 64. A drain re-tests every token against the bound as it then
+    // stands, which only drops tokens that cannot win.
+    auto drain = [&](int base, int cnt) __attribute__((always_inline)) {
+      if (lane < cnt) {
+        const int ei = base + lane;
+        const int xg = q_x[wave][ei];
+        const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          const float lt = q_t[wave][ei * kQG + e], ld = q_d[wave][ei * kQG + e];
+          const int x = xg + e;
+          const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
+          float p = fast_exp2(fmaf(lt, c, -mct)) * ist;
+          if (FILT && lt < tht) p = 0.0f;
+          const float qq = fast_exp2(fmaf(ld, c, -mcd)) * isd;
+          const float mu = (qq >= tau && !(FILT && ld < thd)) ? qq : 0.0f;
+          const float r = fmaxf(p - mu, 0.0f);
+          if (r > 0.0f && r >= pthr) {
+            top2_push(t, div_fast(r, expo32(wd)), x, lt, ld);
+            const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
+            safe = fmaxf(safe, div_fast(rl, expo32_upper(wd)) * (1.0f - kKeyErr));
+          }
+          if (prace && !(lt < tht) && lt * c >= plb) top2_push(tq, lt * c - log2_expo32(wd), x, lt, 0.0f);
+        }
+      }
+    };
+    int qn = 0;  // queued groups, wave-uniform
     auto fold_res = [&](const CH (&xt)[U], const CH (&xd)[U], int v0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        bool live = true;
         if (!DIAG || FILT) {
           float mt = xt[u].get(0);
 #pragma unroll
           for (int e = 1; e < VEC; ++e) mt = fmaxf(mt, xt[u].get(e));
           // r <= p: no token of a vector whose largest p misses pthr is a candidate
-          if (!DIAG && !(fmaf(mt, c, -mct) >= sthr)) continue;
+          if (!DIAG) live = fmaf(mt, c, -mct) >= sthr;
           // every target logit of the vector below the keep-threshold: p = 0, r = 0, and no
           // token takes part in the race over p either
-          if (FILT && mt < tht) continue;
+          if (FILT) live = live && !(mt < tht);
+          if (!DIAG && !__any(live)) continue;  // the whole wave skips the vector
         }
         const int x0 = (v0 + u * kWave) * VEC;
         float rv[VEC], mv[VEC];
@@ -1145,35 +1217,31 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
           bool any = false, anyp = false;
 #pragma unroll
           for (int e = 0; e < G; ++e) {
-            const float p = rv[gg + e], mu = mv[gg + e];
-            rv[gg + e] = fmaxf(p - mu, 0.0f);
-            mv[gg + e] = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
-            if (DIAG) rsum += rv[gg + e];
-            any |= (rv[gg + e] > 0.0f && rv[gg + e] >= pthr);
+            const float r = fmaxf(rv[gg + e] - mv[gg + e], 0.0f);
+            if (DIAG) rsum += r;
+            any |= (r > 0.0f && r >= pthr);
             if (prace) anyp |= !(xt[u].get(gg + e) < tht) && xt[u].get(gg + e) * c >= plb;
           }
-          if (any || anyp) {
-            const int xg = x0 + gg;
-            const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
+          const bool cand = live && (any || anyp);
+          const uint64_t m = __ballot(cand);
+          if (cand) {
+            const int pos = qn + lane_rank(m);
+            q_x[wave][pos] = x0 + gg;
 #pragma unroll
             for (int e = 0; e < G; ++e) {
-              const float r = rv[gg + e];
-              if (r > 0.0f && r >= pthr) {
-                const int x = xg + e;
-                const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
-                top2_push(t, div_fast(r, expo32(wd)), x, xt[u].get(gg + e), xd[u].get(gg + e));
-                safe = fmaxf(safe, div_fast(mv[gg + e], expo32_upper(wd)) * (1.0f - kKeyErr));
-              }
-              if (prace) {
-                const float l = xt[u].get(gg + e);
-                if (!(l < tht) && l * c >= plb) {
-                  const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, (xg + e) & 3);
-                  top2_push(tq, l * c - log2_expo32(wd), xg + e, l, 0.0f);
-                }
-              }
+              q_t[wave][pos * kQG + e] = xt[u].get(gg + e);
+              q_d[wave][pos * kQG + e] = xd[u].get(gg + e);
             }
           }
+          qn = uni(qn + (int)__popcll(m));
         }
+      }
+      // One drain site per fold keeps the unrolled loop small in the instruction cache.
+      while (qn >= kWave) {
+        __builtin_amdgcn_wave_barrier();
+        drain(qn - kWave, kWave);
+        __builtin_amdgcn_wave_barrier();
+        qn -= kWave;
       }
     };
     // Double buffering with an exit only at the bottom (see pass 1).
@@ -1190,6 +1258,10 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       fold_res(tb, db, base + step + lane);
       pthr = fmaxf(pthr, wave_max(safe) * (float)(kEminLow * 0.5));
       if (!DIAG) sthr = sthr_of(pthr);
+    }
+    if (qn > 0) {
+      __builtin_amdgcn_wave_barrier();
+      drain(0, qn);
     }
     part.rsum = DIAG ? wave_sum(rsum) : 0.0f;
     double bk;
@@ -1221,65 +1293,189 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     int bad = 0;
     Top2 t = top2_empty();
     float wbest = -INFINITY;  // best log2 key the wave has drawn so far
+    // A span of at most KR vectors per lane is read once, all of it at once, and held in
+    // registers for both steps below; a longer one is streamed twice (the second time from the
+    // caches).
+    constexpr int KR = VEC == 1 ? 16 : 8;
+    const bool held = sp.end - sp.begin <= KR * kWave;
+    CH hb[KR];
     CH ta[U], tb[U];
-    auto fold_bonus = [&](const CH (&xt)[U], int v0) __attribute__((always_inline)) {
-      if (race) fold_max<false>(a, xt, v0, bad);  // max and NaN / +inf check
-      else fold_max<true>(a, xt, v0, bad);       // ... and the lowest index of the max
-      if (race) {
-        // A token's log2 key is l*c - log2(E) with 2^-24 < E < 16.7, so it lies within
-        // (l*c - 4.06, l*c + 24). The wave's largest l*c so far therefore gives a key of at
-        // least max(l*c) - 4.06, and a token more than 28.1 below that cannot win. The
-        // margins (4.1, 25) absorb fp32 error.
-        const float lb = fmaxf(wbest, wave_max(a.m) * c - 4.1f);
-        float lbest = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int x0 = (v0 + u * kWave) * VEC;
-#pragma unroll
-          for (int gg = 0; gg < VEC; gg += G) {
-            float av[G];
-            bool any = false;
-#pragma unroll
-            for (int e = 0; e < G; ++e) {
-              av[e] = xt[u].get(gg + e) * c;
-              if (FILT && xt[u].get(gg + e) < q.th_t) av[e] = -INFINITY;  // outside p's support
-              any |= av[e] + 25.0f >= lb;
-            }
-            if (any) {
-              const int xg = x0 + gg;
-              const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
-#pragma unroll
-              for (int e = 0; e < G; ++e) {
-                if (av[e] + 25.0f >= lb) {
-                  const int x = xg + e;
-                  const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
-                  const float key = av[e] - log2_expo32(wd);
-                  lbest = fmaxf(lbest, key);
-                  top2_push(t, key, x, xt[u].get(gg + e), 0.0f);
-                }
-              }
-            }
-          }
-        }
-        wbest = fmaxf(wbest, wave_max(lbest));
+    // First the span's maximum (and NaN / +inf check, and for greedy rows the lowest index of
+    // the maximum).
+    if (held) {
+      if (nsteps > 0) {
+        load_chunks<false>(hb, trow, sp.begin, lane, sp.end);
+        mask_chunks(hb, sp.begin, lane, sp.end);
+        fold_max<true>(a, hb, sp.begin + lane, bad);
       }
-    };
-    if (nsteps > 0) load_chunks<false>(ta, trow, sp.begin, lane, sp.end);
-    for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
-      load_chunks<false>(tb, trow, base + step, lane, sp.end);
-      mask_chunks(ta, base, lane, sp.end);
-      fold_bonus(ta, base + lane);
-      load_chunks<false>(ta, trow, base + 2 * step, lane, sp.end);
-      mask_chunks(tb, base + step, lane, sp.end);
-      fold_bonus(tb, base + step + lane);
+    } else {
+      load_chunks<false>(ta, trow, sp.begin, lane, sp.end);
+      for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+        load_chunks<false>(tb, trow, base + step, lane, sp.end);
+        mask_chunks(ta, base, lane, sp.end);
+        fold_max<true>(a, ta, base + lane, bad);
+        load_chunks<false>(ta, trow, base + 2 * step, lane, sp.end);
+        mask_chunks(tb, base + step, lane, sp.end);
+        fold_max<true>(a, tb, base + step + lane, bad);
+      }
     }
     float m;
     float unused;
     int am;
     wave_stat(a, 0.0f, false, m, unused, am);
+    const int am_w = exact_argmax<CH>(trow, a, m);
     part.mref = m;
-    part.gidx = race ? -1 : exact_argmax<CH>(trow, a, m);
+    part.gidx = race ? -1 : am_w;
     part.bad = wave_or(bad);
+    if (race && nsteps > 0) {
+      // Pruning bound. A token's log2 key is l*c - log2(E) with 2^-24 < E < 16.7, so it lies
+      // within (l*c - 4.06, l*c + 24): a token more than 25 below a drawn key cannot win (the
+      // margin absorbs fp32 error). The waves of a request pool their best (logit, token) in
+      // one word with an atomic max, and each takes the key of the best token pooled so far
+      // as its starting bound: on rows with a few large logits, every wave then skips
+      // nearly all of its span. The largest logit is in p's support under every filter.
+      float lb = m * c - 4.1f;
+      uint64_t best = 0;
+      if (am_w >= 0) {
+        const uint64_t mine = pack_best(m, am_w);
+        uint64_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(w.bmax + b),
+                                                    (unsigned long long)mine, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        old = uni64(old);
+        best = old > mine ? old : mine;
+      }
+      if (best != 0) {
+        const float mg = best_logit(best);
+        const int ig = (int)(uint32_t)best;
+        if (__builtin_isfinite(mg) && ig >= 0 && ig < in.V)
+          lb = fmaxf(lb, mg * c - log2_expo32(race_word(in.seed, ig, q.k, b)));
+      }
+      // Candidate groups are queued and drawn 64 at a time, as in the residual race.
+      int qn = 0;  // queued groups, wave-uniform
+      auto drain = [&](int base, int cnt) __attribute__((always_inline)) {
+        float lbest = -INFINITY;
+        if (lane < cnt) {
+          const int ei = base + lane;
+          const int xg = q_x[wave][ei];
+          const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
+#pragma unroll
+          for (int e = 0; e < G; ++e) {
+            const float l = q_t[wave][ei * kQG + e];
+            float av = l * c;
+            if (FILT && l < q.th_t) av = -INFINITY;  // outside p's support
+            if (av + 25.0f >= lb) {
+              const int x = xg + e;
+              const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
+              const float key = av - log2_expo32(wd);
+              lbest = fmaxf(lbest, key);
+              top2_push(t, key, x, l, 0.0f);
+            }
+          }
+        }
+        wbest = fmaxf(wbest, wave_max(lbest));
+        lb = fmaxf(lb, wbest);
+      };
+      // Before its first drain, a wave that pooled early reads the pooled pair again (the
+      // other waves have published by then) and drops the queued groups that the tighter
+      // bound excludes.
+      bool refreshed = false;
+      auto refresh = [&]() __attribute__((always_inline)) {
+        refreshed = true;
+        const uint64_t now = uni64(__hip_atomic_load(reinterpret_cast<unsigned long long*>(w.bmax + b),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (now <= best) return;
+        best = now;
+        const float mg = best_logit(now);
+        const int ig = (int)(uint32_t)now;
+        if (!(__builtin_isfinite(mg) && ig >= 0 && ig < in.V)) return;
+        const float nl = mg * c - log2_expo32(race_word(in.seed, ig, q.k, b));
+        if (!(nl > lb)) return;
+        lb = nl;
+        __builtin_amdgcn_wave_barrier();
+        int kept = 0;
+        for (int base = 0; base < qn; base += kWave) {  // in order, so writes never pass reads
+          const int ei = base + lane;
+          bool keep = false;
+          int xg = 0;
+          float lt[kQG];
+          if (ei < qn) {
+            xg = q_x[wave][ei];
+#pragma unroll
+            for (int e = 0; e < kQG; ++e) {
+              lt[e] = q_t[wave][ei * kQG + e];
+              keep |= lt[e] * c + 25.0f >= lb && !(FILT && lt[e] < q.th_t);
+            }
+          }
+          const uint64_t mk = __ballot(keep);
+          __builtin_amdgcn_wave_barrier();
+          if (keep) {
+            const int pos = kept + lane_rank(mk);
+            q_x[wave][pos] = xg;
+#pragma unroll
+            for (int e = 0; e < kQG; ++e) q_t[wave][pos * kQG + e] = lt[e];
+          }
+          __builtin_amdgcn_wave_barrier();
+          kept = uni(kept + (int)__popcll(mk));
+        }
+        qn = kept;
+      };
+      auto fold_race = [&](const auto& xt, int v0) __attribute__((always_inline)) {
+        constexpr int UU = sizeof(xt) / sizeof(xt[0]);
+#pragma unroll
+        for (int u = 0; u < UU; ++u) {
+          const int x0 = (v0 + u * kWave) * VEC;
+#pragma unroll
+          for (int gg = 0; gg < VEC; gg += G) {
+            bool any = false;
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+              const float l = xt[u].get(gg + e);
+              any |= l * c + 25.0f >= lb && !(FILT && l < q.th_t);
+            }
+            const uint64_t mk = __ballot(any);
+            if (any) {
+              const int pos = qn + lane_rank(mk);
+              q_x[wave][pos] = x0 + gg;
+#pragma unroll
+              for (int e = 0; e < G; ++e) q_t[wave][pos * kQG + e] = xt[u].get(gg + e);
+            }
+            qn = uni(qn + (int)__popcll(mk));
+          }
+        }
+        if (qn >= kWave && !refreshed) refresh();
+        while (qn >= kWave) {  // one drain site per fold (see the residual race)
+          __builtin_amdgcn_wave_barrier();
+          drain(qn - kWave, kWave);
+          __builtin_amdgcn_wave_barrier();
+          qn -= kWave;
+        }
+      };
+      // Then the race.
+      if (held) {
+#pragma unroll
+        for (int k = 0; k < KR; k += U) {
+          CH pair[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) pair[u] = hb[k + u];
+          fold_race(pair, sp.begin + k * kWave + lane);
+        }
+      } else {
+        load_chunks<false>(ta, trow, sp.begin, lane, sp.end);
+        for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+          load_chunks<false>(tb, trow, base + step, lane, sp.end);
+          mask_chunks(ta, base, lane, sp.end);
+          fold_race(ta, base + lane);
+          load_chunks<false>(ta, trow, base + 2 * step, lane, sp.end);
+          mask_chunks(tb, base + step, lane, sp.end);
+          fold_race(tb, base + step + lane);
+        }
+      }
+      if (qn > 0) {
+        __builtin_amdgcn_wave_barrier();
+        drain(0, qn);
+      }
+    }
     if (race) {
       double bk;
       int bi;
@@ -1298,6 +1494,10 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
 
   // ---- the request's last wave: merge the partials and write the outputs
   const P2Part* pp = w.part2 + (int64_t)b * nw;
+  // Every wave of the request has pooled its best pair: leave the word at zero for the next call.
+  if (q.kind == kKindBonus && lane == 0)
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(w.bmax + b), 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   bool invalid = false;
   int token = -1;
   float resid = NAN;
@@ -2477,7 +2677,7 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
          reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
          reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3),
-         reinterpret_cast<int32_t*>(ws + p.off_lazy)};
+         reinterpret_cast<int32_t*>(ws + p.off_lazy), reinterpret_cast<uint64_t*>(ws + p.off_bmax)};
   Outputs out{out_tokens, out_accept_len, diag, stats};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
@@ -2593,7 +2793,7 @@ extern "C" sv_status sv_verify_batch_lazy(const void* target_logits, const void*
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
          reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
          reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3),
-         reinterpret_cast<int32_t*>(ws + p.off_lazy)};
+         reinterpret_cast<int32_t*>(ws + p.off_lazy), reinterpret_cast<uint64_t*>(ws + p.off_bmax)};
   Outputs out{out_tokens, out_accept_len, nullptr, nullptr};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
@@ -2628,7 +2828,7 @@ static sv_status row_sums_run(const void* target_logits, const void* draft_logit
   Work w{reinterpret_cast<WsHeader*>(ws + p.off_hdr), reinterpret_cast<P1Part*>(ws + p.off_part1),
          reinterpret_cast<P2Part*>(ws + p.off_part2), reinterpret_cast<uint32_t*>(ws + p.off_ticket2),
          reinterpret_cast<SumPart*>(ws + p.off_part3), reinterpret_cast<uint32_t*>(ws + p.off_done3),
-         reinterpret_cast<int32_t*>(ws + p.off_lazy)};
+         reinterpret_cast<int32_t*>(ws + p.off_lazy), reinterpret_cast<uint64_t*>(ws + p.off_bmax)};
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;

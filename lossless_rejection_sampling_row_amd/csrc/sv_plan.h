@@ -87,7 +87,7 @@ struct Plan {
   int32_t esize;  // bytes per logit
   int32_t w1max;  // pass 1: most waves that share one row (sizes the partial array)
   int32_t w2max;  // pass 2: most waves that share one request
-  size_t off_hdr, off_part1, off_part2, off_part3, off_lazy, off_theta, off_ticket2, off_done3, total;
+  size_t off_hdr, off_part1, off_part2, off_part3, off_lazy, off_theta, off_ticket2, off_bmax, off_done3, total;
 };
 
 // Build the plan for a shape. Returns SV_OK, or the status describing why the

@@ -873,12 +873,20 @@ __device__ __forceinline__ void add_stats(const Outputs& out, const ReqState& q,
 
 // Write request b's outputs (one wave): the accepted drafts, the last token, -1 after it.
 // A request that fails closed gets -1 everywhere and untested diagnostics.
+// With dt_held, lane j already holds the drafted token of row lo + j (j < 64) in dt_reg, which
+// saves the emitting wave a round trip.
 template <bool FILT = false>
 __device__ __forceinline__ void emit_request(const Inputs& in, const Work& w, const Outputs& out, int b,
-                                             const ReqState& q, bool invalid, int token, float resid, int lane) {
+                                             const ReqState& q, bool invalid, int token, float resid, int lane,
+                                             bool dt_held = false, int dt_reg = 0) {
   for (int j = lane; j < q.n; j += kWave) {
     const int r = q.lo + j;
-    out.tokens[r] = invalid ? -1 : (j < q.k ? in.dt[r] : (j == q.k ? token : -1));
+    int t = -1;
+    if (!invalid) {
+      if (j < q.k) t = (dt_held && j < kWave) ? dt_reg : in.dt[r];
+      else if (j == q.k) t = token;
+    }
+    out.tokens[r] = t;
   }
   if (lane == 0) {
     out.accept_len[b] = invalid ? -1 : q.k;
@@ -1060,7 +1068,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   if (q.kind == kKindGreedyDone) {
     // One-hot p and mu: the residual is empty iff the offered draft argmax is the target argmax.
     const float resid = (q.stop.am_t == q.stop.am_d && 1.0f >= q.tau) ? 0.0f : 1.0f;
-    if (head) emit_request<FILT>(in, w, out, b, q, false, q.stop.am_t, resid, lane);
+    if (head) emit_request<FILT>(in, w, out, b, q, false, q.stop.am_t, resid, lane, q.lo == lo_pre, dt0);
     return;
   }
 
@@ -1196,6 +1204,33 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
           if (!DIAG && !__any(live)) continue;  // the whole wave skips the vector
         }
         const int x0 = (v0 + u * kWave) * VEC;
+        if (!DIAG) {
+          // A candidate needs p >= pthr (r <= p): one test per token in the logit domain, with
+          // no exponential. The drain computes p, mu and r for the queued tokens.
+#pragma unroll
+          for (int gg = 0; gg < VEC; gg += G) {
+            bool any = false;
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+              const float l = xt[u].get(gg + e);
+              any |= fmaf(l, c, -mct) >= sthr && !(FILT && l < tht);
+              if (prace) any |= !(l < tht) && l * c >= plb;
+            }
+            const bool cand = live && any;
+            const uint64_t m = __ballot(cand);
+            if (cand) {
+              const int pos = qn + lane_rank(m);
+              q_x[wave][pos] = x0 + gg;
+#pragma unroll
+              for (int e = 0; e < G; ++e) {
+                q_t[wave][pos * kQG + e] = xt[u].get(gg + e);
+                q_d[wave][pos * kQG + e] = xd[u].get(gg + e);
+              }
+            }
+            qn = uni(qn + (int)__popcll(m));
+          }
+          continue;
+        }
         float rv[VEC], mv[VEC];
         bool gated = false;
 #pragma unroll
@@ -1564,7 +1599,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       token = bi;
     }
   }
-  emit_request<FILT>(in, w, out, b, q, invalid, token, resid, lane);
+  emit_request<FILT>(in, w, out, b, q, invalid, token, resid, lane, q.lo == lo_pre, dt0);
 }
 
 // ====================================================================== lazy verify

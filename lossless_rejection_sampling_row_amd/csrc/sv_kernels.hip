@@ -961,6 +961,23 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// A queued logit: its bf16 bits for bf16 inputs (every logit read from them is a bf16 value,
+// so this is exact), the float itself for fp32 inputs.
+template <typename E>
+struct QLogit;
+template <>
+struct QLogit<uint16_t> {
+  using T = uint16_t;
+  static __device__ __forceinline__ T enc(float f) { return (uint16_t)(__float_as_uint(f) >> 16); }
+  static __device__ __forceinline__ float dec(T h) { return __uint_as_float((uint32_t)h << 16); }
+};
+template <>
+struct QLogit<float> {
+  using T = float;
+  static __device__ __forceinline__ T enc(float f) { return f; }
+  static __device__ __forceinline__ float dec(T f) { return f; }
+};
+
 // The number of lanes below this one whose bit is set in m.
 __device__ __forceinline__ int lane_rank(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -1024,8 +1041,9 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
   constexpr int kQueueCap = queue_cap<VEC, U>();
   __shared__ int q_x[kWavesPerBlock][kQueueCap];
   constexpr int kQG = VEC >= 4 ? 4 : 1;  // tokens per queued group
-  __shared__ float q_t[kWavesPerBlock][kQueueCap * kQG];
-  __shared__ float q_d[kWavesPerBlock][kQueueCap * kQG];
+  using QL = QLogit<E>;
+  __shared__ typename QL::T q_t[kWavesPerBlock][kQueueCap * kQG];
+  __shared__ typename QL::T q_d[kWavesPerBlock][kQueueCap * kQG];
   if (gw >= (int64_t)in.B * in.w2) return;
   const int b = (int)(gw / in.w2);
   const int g = (int)(gw % in.w2);
@@ -1170,7 +1188,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
         const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
 #pragma unroll
         for (int e = 0; e < G; ++e) {
-          const float lt = q_t[wave][ei * kQG + e], ld = q_d[wave][ei * kQG + e];
+          const float lt = QL::dec(q_t[wave][ei * kQG + e]), ld = QL::dec(q_d[wave][ei * kQG + e]);
           const int x = xg + e;
           const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
           float p = fast_exp2(fmaf(lt, c, -mct)) * ist;
@@ -1223,8 +1241,8 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
               q_x[wave][pos] = x0 + gg;
 #pragma unroll
               for (int e = 0; e < G; ++e) {
-                q_t[wave][pos * kQG + e] = xt[u].get(gg + e);
-                q_d[wave][pos * kQG + e] = xd[u].get(gg + e);
+                q_t[wave][pos * kQG + e] = QL::enc(xt[u].get(gg + e));
+                q_d[wave][pos * kQG + e] = QL::enc(xd[u].get(gg + e));
               }
             }
             qn = uni(qn + (int)__popcll(m));
@@ -1264,8 +1282,8 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
             q_x[wave][pos] = x0 + gg;
 #pragma unroll
             for (int e = 0; e < G; ++e) {
-              q_t[wave][pos * kQG + e] = xt[u].get(gg + e);
-              q_d[wave][pos * kQG + e] = xd[u].get(gg + e);
+              q_t[wave][pos * kQG + e] = QL::enc(xt[u].get(gg + e));
+              q_d[wave][pos * kQG + e] = QL::enc(xd[u].get(gg + e));
             }
           }
           qn = uni(qn + (int)__popcll(m));
@@ -1396,7 +1414,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
           const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
 #pragma unroll
           for (int e = 0; e < G; ++e) {
-            const float l = q_t[wave][ei * kQG + e];
+            const float l = QL::dec(q_t[wave][ei * kQG + e]);
             float av = l * c;
             if (FILT && l < q.th_t) av = -INFINITY;  // outside p's support
             if (av + 25.0f >= lb) {
@@ -1438,7 +1456,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
             xg = q_x[wave][ei];
 #pragma unroll
             for (int e = 0; e < kQG; ++e) {
-              lt[e] = q_t[wave][ei * kQG + e];
+              lt[e] = QL::dec(q_t[wave][ei * kQG + e]);
               keep |= lt[e] * c + 25.0f >= lb && !(FILT && lt[e] < q.th_t);
             }
           }
@@ -1448,7 +1466,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
             const int pos = kept + lane_rank(mk);
             q_x[wave][pos] = xg;
 #pragma unroll
-            for (int e = 0; e < kQG; ++e) q_t[wave][pos * kQG + e] = lt[e];
+            for (int e = 0; e < kQG; ++e) q_t[wave][pos * kQG + e] = QL::enc(lt[e]);
           }
           __builtin_amdgcn_wave_barrier();
           kept = uni(kept + (int)__popcll(mk));
@@ -1473,7 +1491,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
               const int pos = qn + lane_rank(mk);
               q_x[wave][pos] = x0 + gg;
 #pragma unroll
-              for (int e = 0; e < G; ++e) q_t[wave][pos * kQG + e] = xt[u].get(gg + e);
+              for (int e = 0; e < G; ++e) q_t[wave][pos * kQG + e] = QL::enc(xt[u].get(gg + e));
             }
             qn = uni(qn + (int)__popcll(mk));
           }

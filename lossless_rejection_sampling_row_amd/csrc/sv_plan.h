@@ -30,6 +30,15 @@ constexpr int kTargetWavesPerCU = 6;
 // them: with 12 per CU, the gated batch above draws in 36 us, against 45 us with 6 per CU
 // and 42 us with 16 per CU.
 constexpr int kTargetWavesPerCU2 = 12;
+// ... but a pass-2 wave takes between 8 KB and 24 KB of its row. Measured on MI355X:
+//  - the gated B=64, V=151936 bf16 batch (latency-bound): 38 to 42 waves per request (spans of
+//    about 8 KB) draw in 28.5 us, against 30.6 us for the 48 that 12 waves per CU would give;
+//  - the ungated B=256, V=256000 bf16 and mixed B=512, V=152064 fp32 batches (bound by the
+//    races' random numbers on flat residuals): 20 to 40 and 24 to 48 waves per request
+//    (spans of 12 to 25 KB) take 452-459 and 420-430 us per step, against 481 and 473 us
+//    for the 12 and 6 waves per request that 12 waves per CU would give.
+constexpr int64_t kMinSpanBytes2 = 8 * kWave * 16;
+constexpr int64_t kMaxSpanBytes2 = 3 * kMinSpanBytes2;
 
 // Row verdict used inside the kernels besides the public SV_ROW_* codes.
 enum : int32_t { kRowInvalid = 5 };

@@ -119,10 +119,10 @@ int main() {
   {
     const Launch l = pick_waves(p, 1536, 1536);  // six waves per CU on 256 CUs
     CHECK(l.w1 == 4 && l.w2 == 24 && l.blocks1 == 256 * 4 / 4 && l.blocks2 == 64 * 24 / 4);
-    const Launch m = pick_waves(p, 1, 1);
-    CHECK(m.w1 == 1 && m.w2 == 1 && m.blocks1 == 64 && m.blocks2 == 16);
+    const Launch m = pick_waves(p, 1, 1);  // a pass-2 span holds at most 24 KB: ceil(151936 * 2 / 24576)
+    CHECK(m.w1 == 1 && m.w2 == 13 && m.blocks1 == 64 && m.blocks2 == 64 * 13 / 4);
     const Launch h = pick_waves(p, 1 << 30, 1 << 30);
-    CHECK(h.w1 == 64 && h.w2 == p.w2max);
+    CHECK(h.w1 == 64 && h.w2 == 38);  // a pass-2 span holds at least 8 KB: ceil(151936 * 2 / 8192)
   }
   CHECK(make_plan(sv_shape{1, 1, 1, SV_F32}, &p) == SV_OK && p.w1max == 1 && p.w2max == 1);
   CHECK(pick_waves(p, 4096, 4096).w1 == 1 && pick_waves(p, 4096, 4096).blocks1 == 1);  // no row to stream

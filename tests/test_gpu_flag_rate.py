@@ -7,6 +7,9 @@ V=151936 bf16 batches in full over 100 seeds each, and 1024 requests each of the
 B=256, T=8, V=256000 and mixed-policy B=512, T=4, V=152064 batches. Summed over all of
 them, flagged requests must number fewer than 1e-4 of the rows. Every other request must
 match the oracle bit for bit. The oracle runs in a host process pool while the GPU works.
+
+The filtered verify is held to the same bar on the gated batch with the serving-style filters
+(top-k, top-p, min-p on both sides, drawn per seed), over 100 seeds.
 """
 import numpy as np
 import pytest
@@ -74,3 +77,34 @@ def test_flag_rate_and_parity_at_scale():
         f"rate {total_flagged / total_rows:.2e} per row")
     assert total_rows >= 60000
     assert total_flagged < 1e-4 * total_rows
+
+
+def test_filtered_flag_rate_and_parity():
+    cfg, seeds = 3, range(100)
+    n = oracle_pool.workers()
+    batch = as_batch(wl.config(cfg))
+    B = len(batch["row_offsets"]) - 1
+    ro = np.asarray(batch["row_offsets"], dtype=np.int64)
+    g = upload(batch)
+    rows = flagged = 0
+    with oracle_pool.make_pool(n) as pool:
+        futs = {s: pool.submit(oracle_pool.oracle_task, cfg, s, list(range(B)), 1000 + s) for s in seeds}
+        for s in seeds:
+            b = dict(batch)
+            b["target_filter"], b["draft_filter"] = wl.sampler_filters(B, rng_seed=1000 + s)
+            gs = dict(g)
+            gs.update({k: v for k, v in upload(b).items() if k.endswith("_filter")})
+            gpu = run_gpu(b, seed=s, gpu=gs, diag=False)
+            flags, lens, toks = futs[s].result()
+            for r in range(B):
+                lo, hi = int(ro[r]), int(ro[r + 1])
+                rows += hi - lo
+                if flags[r]:
+                    flagged += 1
+                    say(f"[flag-rate] filtered seed={s} request {r} flags={int(flags[r])}")
+                    continue
+                assert gpu.out_accept_len[r] == lens[r], (s, r, gpu.out_accept_len[r], lens[r])
+                assert np.array_equal(gpu.out_tokens[lo:hi], toks[lo:hi]), (s, r)
+    say(f"[flag-rate] filtered {wl.CONFIG_NAMES[cfg]}: {len(seeds)} seeds, {rows} rows, {flagged} flagged "
+        f"requests, rate {flagged / rows:.2e} per row")
+    assert flagged < 1e-4 * rows

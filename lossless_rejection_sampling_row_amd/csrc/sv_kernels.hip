@@ -1181,28 +1181,37 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     // drawn 64 at a time, one group per lane: a Philox block costs a wave the same whether
     // one lane needs it or all 64. A drain re-tests every token against the bound as it then
     // stands, which only drops tokens that cannot win.
+    // Draw the group of G tokens starting at xg, with their target and draft logits.
+    auto draw_res = [&](int xg, const float (&lts)[G], const float (&lds)[G]) __attribute__((always_inline)) {
+      const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        const float lt = lts[e], ld = lds[e];
+        const int x = xg + e;
+        const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
+        float p = fast_exp2(fmaf(lt, c, -mct)) * ist;
+        if (FILT && lt < tht) p = 0.0f;
+        const float qq = fast_exp2(fmaf(ld, c, -mcd)) * isd;
+        const float mu = (qq >= tau && !(FILT && ld < thd)) ? qq : 0.0f;
+        const float r = fmaxf(p - mu, 0.0f);
+        if (r > 0.0f && r >= pthr) {
+          top2_push(t, div_fast(r, expo32(wd)), x, lt, ld);
+          const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
+          safe = fmaxf(safe, div_fast(rl, expo32_upper(wd)) * (1.0f - kKeyErr));
+        }
+        if (prace && !(lt < tht) && lt * c >= plb) top2_push(tq, lt * c - log2_expo32(wd), x, lt, 0.0f);
+      }
+    };
     auto drain = [&](int base, int cnt) __attribute__((always_inline)) {
       if (lane < cnt) {
         const int ei = base + lane;
-        const int xg = q_x[wave][ei];
-        const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
+        float lts[G], lds[G];
 #pragma unroll
         for (int e = 0; e < G; ++e) {
-          const float lt = QL::dec(q_t[wave][ei * kQG + e]), ld = QL::dec(q_d[wave][ei * kQG + e]);
-          const int x = xg + e;
-          const uint32_t wd = G == 4 ? word_of(ph, e) : word_of(ph, x & 3);
-          float p = fast_exp2(fmaf(lt, c, -mct)) * ist;
-          if (FILT && lt < tht) p = 0.0f;
-          const float qq = fast_exp2(fmaf(ld, c, -mcd)) * isd;
-          const float mu = (qq >= tau && !(FILT && ld < thd)) ? qq : 0.0f;
-          const float r = fmaxf(p - mu, 0.0f);
-          if (r > 0.0f && r >= pthr) {
-            top2_push(t, div_fast(r, expo32(wd)), x, lt, ld);
-            const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
-            safe = fmaxf(safe, div_fast(rl, expo32_upper(wd)) * (1.0f - kKeyErr));
-          }
-          if (prace && !(lt < tht) && lt * c >= plb) top2_push(tq, lt * c - log2_expo32(wd), x, lt, 0.0f);
+          lts[e] = QL::dec(q_t[wave][ei * kQG + e]);
+          lds[e] = QL::dec(q_d[wave][ei * kQG + e]);
         }
+        draw_res(q_x[wave][ei], lts, lds);
       }
     };
     int qn = 0;  // queued groups, wave-uniform
@@ -1224,25 +1233,49 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
         const int x0 = (v0 + u * kWave) * VEC;
         if (!DIAG) {
           // A candidate needs p >= pthr (r <= p): one test per token in the logit domain, with
-          // no exponential. The drain computes p, mu and r for the queued tokens.
+          // no exponential. On a flat residual nearly every group is a candidate: the wave then
+          // draws the vector's groups in place; otherwise it queues them for the drain, which
+          // computes p, mu and r for the queued tokens.
+          constexpr int NG = VEC / G;
+          bool cg[NG];
+          int ncand = 0;
 #pragma unroll
-          for (int gg = 0; gg < VEC; gg += G) {
+          for (int gi = 0; gi < NG; ++gi) {
             bool any = false;
 #pragma unroll
             for (int e = 0; e < G; ++e) {
-              const float l = xt[u].get(gg + e);
+              const float l = xt[u].get(gi * G + e);
               any |= fmaf(l, c, -mct) >= sthr && !(FILT && l < tht);
               if (prace) any |= !(l < tht) && l * c >= plb;
             }
-            const bool cand = live && any;
-            const uint64_t m = __ballot(cand);
-            if (cand) {
+            cg[gi] = live && any;
+            ncand += (int)__popcll(__ballot(cg[gi]));
+          }
+          if (4 * ncand >= 3 * NG * kWave) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+              if (cg[gi]) {
+                float lts[G], lds[G];
+#pragma unroll
+                for (int e = 0; e < G; ++e) {
+                  lts[e] = xt[u].get(gi * G + e);
+                  lds[e] = xd[u].get(gi * G + e);
+                }
+                draw_res(x0 + gi * G, lts, lds);
+              }
+            }
+            continue;
+          }
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) {
+            const uint64_t m = __ballot(cg[gi]);
+            if (cg[gi]) {
               const int pos = qn + lane_rank(m);
-              q_x[wave][pos] = x0 + gg;
+              q_x[wave][pos] = x0 + gi * G;
 #pragma unroll
               for (int e = 0; e < G; ++e) {
-                q_t[wave][pos * kQG + e] = QL::enc(xt[u].get(gg + e));
-                q_d[wave][pos * kQG + e] = QL::enc(xd[u].get(gg + e));
+                q_t[wave][pos * kQG + e] = QL::enc(xt[u].get(gi * G + e));
+                q_d[wave][pos * kQG + e] = QL::enc(xd[u].get(gi * G + e));
               }
             }
             qn = uni(qn + (int)__popcll(m));

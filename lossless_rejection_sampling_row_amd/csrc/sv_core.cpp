@@ -93,11 +93,15 @@ Launch pick_waves(const Plan& p, int64_t slots1, int64_t slots2) {
   int64_t pow2 = 1;
   while (pow2 * 2 <= w1) pow2 *= 2;
   int64_t w2 = t.w2 > 0 ? t.w2 : p.B > 0 ? slots2 / p.B : 1;
-  if (t.w2 <= 0) {  // spans of 8 KB to 24 KB
+  if (t.w2 <= 0 && p.B > 0) {
+    // Spans of 8 KB to 24 KB, but at least about one wave per compute unit in all (slots2
+    // counts kTargetWavesPerCU2 per unit): a batch of one or two requests still spreads.
     const int64_t row_bytes = (int64_t)p.V * p.esize;
     const int64_t lo = ceil_div(row_bytes, kMaxSpanBytes2), hi = ceil_div(row_bytes, kMinSpanBytes2);
     if (w2 < lo) w2 = lo;
     if (w2 > hi) w2 = hi;
+    const int64_t spread = ceil_div(slots2 / kTargetWavesPerCU2, p.B);
+    if (w2 < spread) w2 = spread;
   }
   l.w1 = (int32_t)pow2;
   l.w2 = (int32_t)(w2 < 1 ? 1 : w2 > p.w2max ? p.w2max : w2);

@@ -122,7 +122,9 @@ int main() {
     const Launch m = pick_waves(p, 1, 1);  // a pass-2 span holds at most 24 KB: ceil(151936 * 2 / 24576)
     CHECK(m.w1 == 1 && m.w2 == 13 && m.blocks1 == 64 && m.blocks2 == 64 * 13 / 4);
     const Launch h = pick_waves(p, 1 << 30, 1 << 30);
-    CHECK(h.w1 == 64 && h.w2 == 38);  // a pass-2 span holds at least 8 KB: ceil(151936 * 2 / 8192)
+    CHECK(h.w1 == 64 && h.w2 == p.w2max);  // about one wave per compute unit beats the 8 KB span
+    const Launch d = pick_waves(p, 4096, 256 * kTargetWavesPerCU2);  // a 256-CU device
+    CHECK(d.w2 == 38);  // a pass-2 span holds at least 8 KB: ceil(151936 * 2 / 8192)
   }
   CHECK(make_plan(sv_shape{1, 1, 1, SV_F32}, &p) == SV_OK && p.w1max == 1 && p.w2max == 1);
   CHECK(pick_waves(p, 4096, 4096).w1 == 1 && pick_waves(p, 4096, 4096).blocks1 == 1);  // no row to stream

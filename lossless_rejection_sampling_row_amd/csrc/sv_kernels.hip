@@ -1900,6 +1900,7 @@ struct FilterSmem {
   float seg_mass[kSegCap];  // with top-p alone: sum of exp2((l - seg_max) * c) over the segment
   int seg_list[kSegCap];    // the segments that hold candidates
   double red[kFiltWaves];
+  int wcount[kFiltWaves];   // per-wave counts of an ordered compaction
   int n_cand, first, n_seg;
 };
 
@@ -1975,7 +1976,7 @@ __device__ __forceinline__ void for_each_logit(const E* row, int nvec, F f) {
 
 // Number of logits >= v.
 template <typename E, int VEC>
-__device__ __noinline__ double count_ge(const E* row, int nvec, float v, FilterSmem& s) {
+__device__ __forceinline__ double count_ge(const E* row, int nvec, float v, FilterSmem& s) {
   int n = 0;
   for_each_logit<E, VEC>(row, nvec, [&](float x) __attribute__((always_inline)) { n += !(x < v); });
   return block_sum((double)n, s);
@@ -1983,7 +1984,7 @@ __device__ __noinline__ double count_ge(const E* row, int nvec, float v, FilterS
 
 // fp64 mass of the logits >= v: sum of exp((l - m) / T).
 template <typename E, int VEC>
-__device__ __noinline__ double mass_ge(const E* row, int nvec, float v, float m, double T, FilterSmem& s) {
+__device__ __forceinline__ double mass_ge(const E* row, int nvec, float v, float m, double T, FilterSmem& s) {
   double t = 0.0;
   for_each_logit<E, VEC>(row, nvec, [&](float x) __attribute__((always_inline)) {
     if (!(x < v)) t += exp(((double)x - (double)m) / T);
@@ -2197,19 +2198,33 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // reaches the bound; with sum_rest the other segments' mass comes from their records. Each
   // wave reads kFiltLoads listed segments per round trip.
   auto gather_segments = [&](const float lo, const bool sum_rest, double& rest) __attribute__((always_inline)) {
-    if (threadIdx.x == 0) {
-      s.n_cand = 0;
-      s.n_seg = 0;
-    }
-    __syncthreads();
+    if (threadIdx.x == 0) s.n_cand = 0;
+    // The listed segments keep their row order (a ballot per wave and a count over the
+    // waves), so every run hands each wave and lane the same segments and sums the same
+    // masses in the same order.
     double tl = 0.0;
-    for (int i = threadIdx.x; i < nseg; i += kFiltBlock) {
-      const float sm = s.seg_max[i];
-      if (!(sm < lo)) s.seg_list[atomicAdd(&s.n_seg, 1)] = i;
-      else if (sum_rest && sm > -INFINITY) tl += (double)s.seg_mass[i] * (double)fast_exp2((sm - m) * c);
+    int ns = 0;  // segments listed so far, the same in every thread
+    for (int base = 0; base < nseg; base += kFiltBlock) {
+      const int i = base + (int)threadIdx.x;
+      bool take = false;
+      if (i < nseg) {
+        const float sm = s.seg_max[i];
+        take = !(sm < lo);
+        if (!take && sum_rest && sm > -INFINITY) tl += (double)s.seg_mass[i] * (double)fast_exp2((sm - m) * c);
+      }
+      const uint64_t mk = __ballot(take);
+      if (lane == 0) s.wcount[wave] = (int)__popcll(mk);
+      __syncthreads();
+      int before = ns, total = 0;
+#pragma unroll
+      for (int w = 0; w < kFiltWaves; ++w) {
+        before += w < wave ? s.wcount[w] : 0;
+        total += s.wcount[w];
+      }
+      if (take) s.seg_list[before + lane_rank(mk)] = i;
+      ns += total;
+      __syncthreads();
     }
-    __syncthreads();
-    const int ns = s.n_seg;
     for (int i0 = wave; i0 < ns; i0 += kFiltWaves * kFiltLoads) {
       Chunk<E, VEC> x[kFiltLoads];
       bool ok[kFiltLoads];

@@ -407,40 +407,39 @@ __device__ __forceinline__ void wave_top2(Top2& t) {
 // for its stores to complete before it takes the ticket, so the wave that draws the last
 // ticket reads complete records.
 
-__device__ __forceinline__ void store_word(uint32_t* p, uint32_t v) {
+// Records of 8-byte words move as 64-bit agent-scope atomic stores and loads.
+__device__ __forceinline__ void store_dword2(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t load_word(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t load_dword2(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int N>
-struct Words {
-  uint32_t w[N];
+struct Dwords {
+  uint64_t w[N];
 };
 
 template <class T>
-__device__ __forceinline__ void publish(T* dst, const T& v) {
-  static_assert(sizeof(T) % 4 == 0, "records are made of 4-byte words");
-  constexpr int n = sizeof(T) / 4;
-  const Words<n> w = __builtin_bit_cast(Words<n>, v);
-  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+__device__ __forceinline__ void publish64(T* dst, const T& v) {
+  static_assert(sizeof(T) % 8 == 0 && alignof(T) >= 8, "records of 8-byte words");
+  constexpr int n = sizeof(T) / 8;
+  const Dwords<n> w = __builtin_bit_cast(Dwords<n>, v);
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
 #pragma unroll
-  for (int i = 0; i < n; ++i) store_word(d + i, w.w[i]);
+  for (int i = 0; i < n; ++i) store_dword2(d + i, w.w[i]);
 }
 
 template <class T>
-__device__ __forceinline__ T read_record(const T* src) {
-  constexpr int n = sizeof(T) / 4;
-  Words<n> w;
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+__device__ __forceinline__ T read_record64(const T* src) {
+  constexpr int n = sizeof(T) / 8;
+  Dwords<n> w;
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
 #pragma unroll
-  for (int i = 0; i < n; ++i) w.w[i] = load_word(s + i);
+  for (int i = 0; i < n; ++i) w.w[i] = load_dword2(s + i);
   return __builtin_bit_cast(T, w);
 }
 
-// Arrive at a counter shared by `total` waves. Returns true in the wave that arrives last.
-// The counter wraps back to zero on the last arrival, ready for the next call.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, int lane) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's published records have completed

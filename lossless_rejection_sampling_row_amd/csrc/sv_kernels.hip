@@ -1575,7 +1575,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     }
   }
 
-  if (lane == 0) publish(&w.part2[(int64_t)b * nw + g], part);
+  if (lane == 0) publish64(&w.part2[(int64_t)b * nw + g], part);
   if (!arrive_last(&w.t2[b], (uint32_t)nw, lane)) return;
 
   // ---- the request's last wave: merge the partials and write the outputs
@@ -1591,7 +1591,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     double R = 0.0, bk = -1.0;
     int bi = INT32_MAX;
     for (int i = lane; i < nw; i += kWave) {
-      const P2Part c2 = read_record(pp + i);
+      const P2Part c2 = read_record64(pp + i);
       if (DIAG) R += (double)c2.rsum;
       if (c2.idx >= 0 && beats(c2.key, c2.idx, bk, bi)) {
         bk = c2.key;
@@ -1609,7 +1609,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
       double pk = -INFINITY;
       int pi = INT32_MAX;
       for (int i = lane; i < nw; i += kWave) {
-        const P2Part c2 = read_record(pp + i);
+        const P2Part c2 = read_record64(pp + i);
         if (c2.pidx >= 0 && beats(c2.pkey, c2.pidx, pk, pi)) {
           pk = c2.pkey;
           pi = c2.pidx;
@@ -1626,7 +1626,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     double bk = -INFINITY;
     int bi = INT32_MAX;
     for (int i = lane; i < nw; i += kWave) {
-      const P2Part c2 = read_record(pp + i);
+      const P2Part c2 = read_record64(pp + i);
       M = fmaxf(M, c2.mref);
       bad |= c2.bad;
       if (c2.idx >= 0 && beats(c2.key, c2.idx, bk, bi)) {
@@ -1641,7 +1641,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     if (q.kind == kKindGreedyBonus) {
       int gi = INT32_MAX;
       for (int i = lane; i < nw; i += kWave) {
-        const P2Part c2 = read_record(pp + i);
+        const P2Part c2 = read_record64(pp + i);
         if (c2.mref == M && c2.gidx >= 0) gi = min(gi, c2.gidx);
       }
       token = wave_min(gi);

@@ -3,8 +3,8 @@
 // The record types below live in the caller's workspace. Their layouts are
 // fixed here so that the kernels and the host-side size computation agree.
 // Pass 1's partials reach pass 2 across the kernel boundary. Pass 2's partials
-// move between its own workgroups word by word with agent-scope atomics, so
-// their fields are 4-byte words (a double counts as two).
+// move between its own workgroups as 8-byte words with agent-scope atomics, so
+// their size is a multiple of 8 bytes.
 #pragma once
 
 #include <stddef.h>

@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "sv_device.h"
 #include "sv_plan.h"
@@ -1181,8 +1182,10 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
     // drawn 64 at a time, one group per lane: a Philox block costs a wave the same whether
     // one lane needs it or all 64. A drain re-tests every token against the bound as it then
     // stands, which only drops tokens that cannot win.
-    // Draw the group of G tokens starting at xg, with their target and draft logits.
-    auto draw_res = [&](int xg, const float (&lts)[G], const float (&lds)[G]) __attribute__((always_inline)) {
+    // Draw the group of G tokens starting at xg, with their target and draft logits. With
+    // raise, the drawn keys also raise the pruning bound (a dense draw skips that: on a flat
+    // residual the bound prunes next to nothing).
+    auto draw_res = [&](int xg, const float (&lts)[G], const float (&lds)[G], auto raise) __attribute__((always_inline)) {
       const Philox4 ph = philox4x32_10((uint32_t)(xg >> 2), kTagRace, (uint32_t)q.k, (uint32_t)b, k0, k1);
 #pragma unroll
       for (int e = 0; e < G; ++e) {
@@ -1196,8 +1199,10 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
         const float r = fmaxf(p - mu, 0.0f);
         if (r > 0.0f && r >= pthr) {
           top2_push(t, div_fast(r, expo32(wd)), x, lt, ld);
-          const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
-          safe = fmaxf(safe, div_fast(rl, expo32_upper(wd)) * (1.0f - kKeyErr));
+          if (decltype(raise)::value) {
+            const float rl = fmaf(p, 1.0f - kKeyErr, -mu * (1.0f + kKeyErr));  // at most the exact residual
+            safe = fmaxf(safe, div_fast(rl, expo32_upper(wd)) * (1.0f - kKeyErr));
+          }
         }
         if (prace && !(lt < tht) && lt * c >= plb) top2_push(tq, lt * c - log2_expo32(wd), x, lt, 0.0f);
       }
@@ -1211,7 +1216,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
           lts[e] = QL::dec(q_t[wave][ei * kQG + e]);
           lds[e] = QL::dec(q_d[wave][ei * kQG + e]);
         }
-        draw_res(q_x[wave][ei], lts, lds);
+        draw_res(q_x[wave][ei], lts, lds, std::true_type{});
       }
     };
     int qn = 0;  // queued groups, wave-uniform
@@ -1261,7 +1266,7 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(Inputs in, Work w, Output
                   lts[e] = xt[u].get(gi * G + e);
                   lds[e] = xd[u].get(gi * G + e);
                 }
-                draw_res(x0 + gi * G, lts, lds);
+                draw_res(x0 + gi * G, lts, lds, std::false_type{});
               }
             }
             continue;

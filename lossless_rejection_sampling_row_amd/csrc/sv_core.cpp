@@ -38,27 +38,39 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   const int64_t w = row_bytes / (2 * kBatchBytes);
   q.w1max = q.w2max = (int32_t)(w < 1 ? 1 : w > kMaxWavesPerRow ? kMaxWavesPerRow : w);
   if ((int64_t)q.R * q.w1max > INT32_MAX || (int64_t)q.B * q.w2max > INT32_MAX) return SV_E_UNSUPPORTED;
+  // The persistent part first: the header, the lazy verify's per-request stop flags, the
+  // filtered verify's keep-thresholds and the counters that every call leaves at zero. Then
+  // the per-call part, which one call writes before it reads: the partial records of passes
+  // 1 and 2 and of the acceptance sums, or, earlier in a filtered call, the filter chain's
+  // segment records and fallback flags (the two sets are never live at once).
   size_t off = 0;
   q.off_hdr = off;
   off += sizeof(WsHeader);
-  q.off_part1 = off = align_up(off, 256);
+  q.off_lazy = off = align_up(off, 256);
+  off += (size_t)q.B * sizeof(int32_t);
+  q.off_theta = off = align_up(off, 256);  // [R] (target, draft)
+  off += (size_t)q.R * 2 * sizeof(float);
+  q.off_ticket2 = off = align_up(off, 256);  // pass 2's request tickets
+  off += (size_t)q.B * sizeof(uint32_t);
+  q.off_bmax = off = align_up(off, 8);  // the bonus race's per-request best (logit, token)
+  off += (size_t)q.B * sizeof(uint64_t);
+  q.off_done3 = off;  // the acceptance sums' per-row done flags
+  off += (size_t)q.R * sizeof(uint32_t);
+  q.off_trans = off = align_up(off, 256);
+  q.off_part1 = off;
   off += (size_t)q.R * q.w1max * sizeof(P1Part);
   q.off_part2 = off = align_up(off, 256);
   off += (size_t)q.B * q.w2max * sizeof(P2Part);
   q.off_part3 = off = align_up(off, 256);
   off += (size_t)q.R * q.w1max * sizeof(SumPart);
-  q.off_lazy = off = align_up(off, 256);  // the lazy verify's per-request stop flags
-  off += (size_t)q.B * sizeof(int32_t);
-  q.off_theta = off = align_up(off, 256);  // the filtered verify's keep-thresholds: [R] (target, draft)
-  off += (size_t)q.R * 2 * sizeof(float);
-  // Counters that every call leaves at zero: pass 2's request tickets, then the acceptance
-  // sums' per-row done flags.
-  q.off_ticket2 = off = align_up(off, 256);
-  off += (size_t)q.B * sizeof(uint32_t);
-  q.off_bmax = off = align_up(off, 8);  // the bonus race's per-request best (logit, token)
-  off += (size_t)q.B * sizeof(uint64_t);
-  q.off_done3 = off;
-  off += (size_t)q.R * sizeof(uint32_t);
+  const size_t end_parts = off;
+  const int64_t nseg = ceil_div((int64_t)s.V, kSegLogits);
+  q.nseg = nseg <= kSegCap ? (int32_t)nseg : 0;
+  q.off_seg = off = q.off_trans;
+  off += (size_t)q.R * 2 * q.nseg * sizeof(SegRec);
+  q.off_fb = off = align_up(off, 256);
+  off += (size_t)q.R * 2 * sizeof(int32_t);
+  off = off > end_parts ? off : end_parts;
   q.total = align_up(off, 256);
   *p = q;
   return SV_OK;

@@ -57,6 +57,12 @@ struct FilterSide {
 struct FilterArgs {
   FilterSide side[2];  // target, draft
   float* theta;        // [R][2] keep-thresholds, written by thresholds_kernel
+  // With segment records (16-byte rows of at most kSegCap segments): the records, [R][2][nseg],
+  // and per row and side a flag that sends it to thresholds_kernel (1) or not (0). Without
+  // (fb null), thresholds_kernel handles every row and side.
+  SegRec* seg = nullptr;
+  int32_t* fb = nullptr;
+  int32_t nseg = 0;
 };
 
 struct Inputs {
@@ -1885,7 +1891,8 @@ __global__ __launch_bounds__(kBlock) void merge_sums_kernel(Inputs in, Work w, f
 //    masses. Exact; the second is slow. Peaked rows keep the window small.
 constexpr int kFiltBlock = 512;  // threads per (row, side); at most 80 VGPRs: 3 workgroups per CU fit
 constexpr int kFiltWaves = kFiltBlock / kWave;
-constexpr int kCandCap = 8192;  // candidate logits one workgroup sorts in LDS
+constexpr int kCandCap = 8192;     // candidate logits one workgroup sorts in LDS
+constexpr int kFiltSegCap = 1024;  // segments one workgroup keeps records of in LDS
 
 // Total order on non-NaN floats as int32: order_key(a) < order_key(b) iff a < b, with -0
 // just below +0.
@@ -1895,15 +1902,14 @@ __device__ __forceinline__ int32_t order_key(float f) {
 }
 __device__ __forceinline__ float key_float(int32_t k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
 
-constexpr int kSegCap = 1024;   // segment records one workgroup keeps in LDS
 
 // A segment is the kWave vectors one wave instruction of walk_row reads: vectors
 // [kWave * s, kWave * s + kWave) of the row.
 struct FilterSmem {
   float cand[kCandCap];
-  float seg_max[kSegCap];   // each segment's largest logit
-  float seg_mass[kSegCap];  // with top-p alone: sum of exp2((l - seg_max) * c) over the segment
-  int seg_list[kSegCap];    // the segments that hold candidates
+  float seg_max[kFiltSegCap];   // each segment's largest logit
+  float seg_mass[kFiltSegCap];  // with top-p alone: sum of exp2((l - seg_max) * c) over the segment
+  int seg_list[kFiltSegCap];    // the segments that hold candidates
   double red[kFiltWaves];
   int wcount[kFiltWaves];   // per-wave counts of an ordered compaction
   int n_cand, first, n_seg;
@@ -2011,11 +2017,9 @@ __device__ float bisect_float(float lo, float hi, P pred) {
   return key_float((int32_t)a);
 }
 
+// Keep-threshold of row r, side `side`, by the whole workgroup.
 template <typename E, int VEC>
-__global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6))) void thresholds_kernel(Inputs in, FilterArgs fa) {
-  __shared__ FilterSmem s;
-  const int r = blockIdx.x;
-  const int side = blockIdx.y;
+__device__ __forceinline__ void thresholds_row(const Inputs& in, const FilterArgs& fa, int r, int side, FilterSmem& s) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   float* out = fa.theta + 2 * (int64_t)r + side;
@@ -2070,8 +2074,8 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // Segment records bound the candidates for top-k when k is at most the segment count, and
   // for top-p alone; the gather then reads only the segments that can hold candidates.
   const int nseg = (nvec + kWave - 1) / kWave;
-  const bool seg_k = topk && fp.k <= nseg && nseg <= kSegCap;
-  const bool seg_p = !topk && topp && nseg <= kSegCap;
+  const bool seg_k = topk && fp.k <= nseg && nseg <= kFiltSegCap;
+  const bool seg_p = !topk && topp && nseg <= kFiltSegCap;
   const bool segs = seg_k || seg_p;
   // ---- pass A: maximum and validity; each thread's largest logit; each segment's largest
   //      logit and, with top-p alone, its mass relative to that logit
@@ -2365,6 +2369,23 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   if (threadIdx.x == 0) *out = fmaxf(fmaxf(th_k, th_p), th_m);
 }
 
+// Without segment records (SENT false): workgroup i takes row i / 2, side i % 2. After the
+// record kernels (SENT true): a smaller grid takes, in turn, the rows and sides they sent
+// back (fb set).
+template <typename E, int VEC, bool SENT>
+__global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(SENT ? 4 : 6))) void thresholds_kernel(Inputs in, FilterArgs fa) {
+  __shared__ FilterSmem s;
+  if (!SENT) {
+    thresholds_row<E, VEC>(in, fa, (int)(blockIdx.x >> 1), (int)(blockIdx.x & 1), s);
+    return;
+  }
+  for (int rs = blockIdx.x; rs < 2 * in.R; rs += gridDim.x) {
+    if (fa.fb[rs] == 0) continue;  // the same for the whole workgroup
+    thresholds_row<E, VEC>(in, fa, rs >> 1, rs & 1, s);
+    __syncthreads();  // the next row reuses s
+  }
+}
+
 // ====================================================================== sampler-match rule
 
 // The comparison rule of mlxcel PR #992, section The premise correction: every tested row
@@ -2575,6 +2596,415 @@ __global__ __launch_bounds__(kBlock) void match_emit_kernel(Inputs in, Work w, c
   if (lane == 0) out.accept_len[b] = stop;
 }
 
+// ====================================================================== filter chain: segment records
+
+// The filter chain's thresholds in three launches when rows are read in 16-byte vectors and
+// hold at most kSegCap segments (thresholds_kernel alone otherwise):
+//  - seg_records_kernel streams every row and side that has an active filter, nw waves each,
+//    and writes one SegRec per segment: what thresholds_kernel's pass A kept in LDS;
+//  - thresholds_finish_kernel takes one wave per row and side and decides the thresholds from
+//    the records as thresholds_kernel does after its pass A (the candidate bound, the gather
+//    of the listed segments, the sort, the top-p scan), with wave-level sorts and scans in
+//    LDS instead of workgroup barriers;
+//  - thresholds_kernel then runs only for the rows and sides the finish sent back: top-k
+//    beyond the segment count, more than kFinCap candidates, or a window that holds less
+//    than top_p of the mass (its exact fallbacks).
+
+// A record's segment holds kSegLogits logits, SV 16-byte vectors per lane of a wave (one of
+// bf16, two of fp32): lane l's v-th vector of segment sg is vector (sg * SV + v) * kWave + l
+// of the row.
+
+template <typename E, int VEC>
+__global__ __launch_bounds__(kBlock) void seg_records_kernel(Inputs in, FilterArgs fa, int nw) {
+  constexpr int SV = kSegLogits / (kWave * VEC);
+  static_assert(SV >= 1 && SV * kWave * VEC == kSegLogits, "segment shape");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (gw >= (int64_t)in.R * 2 * nw) return;
+  const int rs = (int)(gw / nw), g = (int)(gw % nw);
+  const int r = rs >> 1, side = rs & 1;
+  const int b = uni(request_of_row(in, r));
+  const float T = in.temp[b];
+  const FilterParams fp = filter_params(fa.side[side], b);
+  const bool topk = fp.k > 0 && fp.k < in.V, topp = fp.top_p < 1.0f, minp = fp.min_p > 0.0f;
+  if (!(T > 0.0f) || !temperature_ok(T) || !filter_valid(fp) || !(topk || topp || minp)) return;
+  const bool mass = topp && !topk;
+  const float c = scale_of(T);
+  const int nseg = fa.nseg, nvec = in.V / VEC;
+  const int per = (nseg + nw - 1) / nw;
+  const int s0 = min(g * per, nseg), s1 = min(s0 + per, nseg);
+  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
+  SegRec* rec = fa.seg + (int64_t)rs * nseg;
+  using CH = Chunk<E, VEC>;
+  constexpr int U = 4 / SV;  // segments per step (four vectors per lane), two steps in flight
+  auto vec_of = [&](int sg, int v) __attribute__((always_inline)) { return (sg * SV + v) * kWave + lane; };
+  auto load = [&](CH (&x)[U][SV], int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)  // past the wave's last segment: that segment again (a cache hit)
+#pragma unroll
+      for (int v = 0; v < SV; ++v) x[u][v].load_nt(row + (int64_t)min(vec_of(min(sb + u, s1 - 1), v), nvec - 1) * VEC);
+  };
+  auto fold = [&](const CH (&x)[U][SV], int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sg = sb + u;
+      if (sg >= s1) break;  // wave-uniform
+      float vm = -INFINITY;
+      int bad = 0;
+#pragma unroll
+      for (int v = 0; v < SV; ++v) {
+        if (vec_of(sg, v) < nvec) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float y = x[u][v].get(e);
+            vm = fmaxf(vm, y);
+            bad |= (int)(__builtin_isnan(y) || y == INFINITY);
+          }
+        }
+      }
+      const float sm = wave_max(bad ? INFINITY : vm);  // +inf marks an invalid segment
+      float ms = 0.0f;
+      if (mass && sm > -INFINITY && sm < INFINITY) {
+#pragma unroll
+        for (int v = 0; v < SV; ++v) {
+          if (vec_of(sg, v) < nvec) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ms += fast_exp2((x[u][v].get(e) - sm) * c);
+          }
+        }
+        ms = wave_sum(ms);
+      }
+      if (lane == 0) rec[sg] = SegRec{sm, ms};
+    }
+  };
+  CH xa[U][SV], xb[U][SV];
+  if (s0 < s1) load(xa, s0);
+  for (int sb = s0; sb < s1; sb += 2 * U) {
+    load(xb, sb + U);
+    fold(xa, sb);
+    load(xa, sb + 2 * U);
+    fold(xb, sb + U);
+  }
+}
+
+// Order one wave's LDS writes before its later LDS reads by other lanes: the LDS serves a
+// wave's operations in issue order, so only the compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+constexpr int kRecordWaves = 10240;  // seg_records_kernel's target grid, in waves
+constexpr int kFinWaves = 4;         // waves per row and side in thresholds_finish_kernel
+constexpr int kFinCap = 256;         // candidates a row and side keeps
+constexpr int kFinVecs = 8;          // 16-byte vectors per lane one gather step stages
+
+// Largest v in [lo, hi] with pred(v), pred monotone (true below some point, false above) and
+// true at lo, found by bisection over order_key(v) / 2^S: with bf16 data (S = 16) every probe
+// lies just below or on a bf16 value, so {x >= v} over the data is decided in 16 steps.
+template <int S, class P>
+__device__ float bisect_key(float lo, float hi, P pred) {
+  if (pred(hi)) return hi;
+  int64_t a = (int64_t)(order_key(lo) >> S), z = (int64_t)(order_key(hi) >> S) + 1;
+  while (z - a > 1) {
+    const int64_t mid = a + (z - a) / 2;
+    if (pred(key_float((int32_t)(mid * ((int64_t)1 << S))))) a = mid;
+    else z = mid;
+  }
+  return key_float((int32_t)(a * ((int64_t)1 << S)));
+}
+
+// kFinWaves waves per row and side (grid 2R). The kernel runs once per row and side, so its
+// instructions come cold from L2: the code keeps to short loops. Every wave keeps the
+// records of segments lane, lane + 64, ... in registers and takes the same decisions up to
+// the gather; the gather splits the listed segments over the waves (loads staged in LDS,
+// then one vector per loop step); wave 0 then decides the thresholds alone. Selections by
+// value are bisections over the float order (bisect_key) whose steps count with ballots: the
+// k-th largest value is the largest v that at least k values reach. top-p's threshold is the
+// largest candidate x whose candidates >= x hold at least top_p times S1: every lane sums,
+// for its own candidates, the masses of all candidates at or above them.
+template <typename E, int VEC>
+__global__ __launch_bounds__(kFinWaves * kWave) void thresholds_finish_kernel(Inputs in, FilterArgs fa) {
+  using CH = Chunk<E, VEC>;
+  constexpr int RS = kSegCap / kWave;  // record slots per lane
+  constexpr int KS = sizeof(E) == 2 ? 16 : 0;  // bisection granularity: bf16 values
+  constexpr int SV = kSegLogits / (kWave * VEC);
+  constexpr int NS = kFinVecs / SV;  // listed segments per wave and gather step
+  __shared__ int s_list[kSegCap];               // the segments to gather, in row order
+  __shared__ CH s_stage[kFinWaves][kFinVecs][kWave];
+  __shared__ float s_cand[kFinWaves][kFinCap];  // each wave's candidates, in gather order
+  __shared__ float s_all[kFinCap];              // all of them, wave 0's first
+  __shared__ double s_e[kFinCap];               // masses exp((x - m) / T), 0 below the base
+  __shared__ int s_cnt[kFinWaves];
+  __shared__ double s_rest[kFinWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int rs = blockIdx.x, r = rs >> 1, side = rs & 1;
+  float* out = fa.theta + rs;  // theta is [R][2]
+  int32_t* fb = fa.fb + rs;
+  const int b = uni(request_of_row(in, r));
+  const float T = in.temp[b];
+  const FilterParams fp = filter_params(fa.side[side], b);
+  const bool topk = fp.k > 0 && fp.k < in.V, topp = fp.top_p < 1.0f, minp = fp.min_p > 0.0f;
+  // Every exit before the gather is taken by the whole workgroup alike.
+  auto done = [&](float th, int back) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) {
+      if (!back) *out = th;
+      *fb = back;
+    }
+  };
+  if (!(T > 0.0f) || !temperature_ok(T) || !filter_valid(fp) || !(topk || topp || minp)) {
+    done(-INFINITY, 0);
+    return;
+  }
+  const int nseg = fa.nseg;
+  if (topk && fp.k > nseg) {
+    done(0.0f, 1);
+    return;
+  }
+  const bool rest_on = topp && !topk;  // top-p alone: S1 is the whole row's mass
+  const SegRec* rec = fa.seg + (int64_t)rs * nseg;
+  float smax[RS], smass[RS];
+  float mx = -INFINITY;
+  int bad = 0;
+#pragma unroll
+  for (int t = 0; t < RS; ++t) {
+    smax[t] = -INFINITY;
+    smass[t] = 0.0f;
+    if (t * kWave + lane < nseg) {
+      const SegRec q = rec[t * kWave + lane];
+      smax[t] = q.max;
+      smass[t] = q.mass;
+    }
+    bad |= (int)!(smax[t] < INFINITY);
+    mx = fmaxf(mx, smax[t]);
+  }
+  const float m = wave_max(mx);
+  if (wave_or(bad) != 0 || m == -INFINITY) {
+    done(INFINITY, 0);
+    return;
+  }
+  const double Td = (double)T;
+  // min-p: the smallest float y with (y - m) / T >= ln(min_p), in fp64 (as thresholds_kernel).
+  float th_m = -INFINITY;
+  if (minp) {
+    const double lm = log((double)fp.min_p);
+    auto keep = [&](float y) { return ((double)y - (double)m) / Td >= lm; };
+    float y = (float)((double)m + Td * lm);
+    for (int it = 0; it < 64 && !keep(y); ++it) y = nextafterf(y, INFINITY);
+    for (int it = 0; it < 64 && keep(nextafterf(y, -INFINITY)); ++it) y = nextafterf(y, -INFINITY);
+    th_m = y;
+  }
+  if (!topk && !topp) {
+    done(th_m, 0);
+    return;
+  }
+  const float c = scale_of(T);
+  // The candidate bound lo: every logit at or above the threshold to find reaches it.
+  //  - top-k: the k-th largest segment maximum (k segments hold a logit that reaches it).
+  //  - top-p alone: start from the window bound (as thresholds_kernel), then raise it to the
+  //    largest v at which the records still prove that the logits >= v hold top_p of the
+  //    row's mass: those in segments whose maximum reaches v hold at least their segments'
+  //    mass less kSegLogits * exp((v - m) / T) per segment. The records' masses are fp32
+  //    sums, so the proof keeps a margin of 2e-4 of the row's mass; the top-p search below
+  //    still checks that the candidates reach top_p.
+  float f[RS];  // top-p alone: exp2((segment max - m) * c), each segment's scale to m
+  float lo;
+  if (topk) {
+    lo = bisect_key<KS>(-INFINITY, m, [&](float v) {
+      int n = 0;
+#pragma unroll
+      for (int t = 0; t < RS; ++t) n += (int)__popcll(__ballot(!(smax[t] < v)));
+      return n >= fp.k;
+    });
+  } else {
+    float Mf[RS];
+    double S = 0.0;
+#pragma unroll
+    for (int t = 0; t < RS; ++t) {
+      f[t] = smax[t] > -INFINITY ? fast_exp2((smax[t] - m) * c) : 0.0f;
+      Mf[t] = smass[t] * f[t];
+      S += (double)smass[t] * (double)f[t];
+    }
+    S = wave_sum(S);
+    const float W = log2f((float)in.V / (1.0f - fp.top_p)) + 1.0f;
+    const double need = (double)fp.top_p * S + 2e-4 * S;
+    lo = bisect_key<KS>(m - (W + 0.01f) / c, m, [&](float v) {
+      float h = 0.0f;
+      int n = 0;
+#pragma unroll
+      for (int t = 0; t < RS; ++t) {
+        const bool on = !(smax[t] < v);
+        h += on ? Mf[t] : 0.0f;
+        n += (int)__popcll(__ballot(on));
+      }
+      const double held = (double)wave_sum(h);
+      return held - (double)n * (double)kSegLogits * exp(((double)v - (double)m) / Td) >= need;
+    });
+  }
+  // The segments that can hold candidates, in row order (listed by wave 0); with top-p alone
+  // the others' mass (summed by wave 0).
+  double tl = 0.0;
+  int ns = 0;
+#pragma unroll
+  for (int t = 0; t < RS; ++t) {
+    const bool real = t * kWave + lane < nseg;
+    const bool take = real && !(smax[t] < lo);
+    if (wave == 0 && rest_on && real && !take) tl += (double)smass[t] * (double)f[t];
+    const uint64_t mk = __ballot(take);
+    if (wave == 0 && take) s_list[ns + lane_rank(mk)] = t * kWave + lane;
+    ns += (int)__popcll(mk);
+  }
+  __syncthreads();
+  // Gather the logits >= lo: wave w takes listed segments w, w + kFinWaves, ..., NS at a
+  // time. A vector whose lanes hold at most one candidate each stores each lane's largest
+  // logit at the lane's rank; otherwise one ballot per element.
+  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
+  const int nvec = in.V / VEC;
+  float* cand = s_cand[wave];
+  auto vec_of = [&](int i0, int q) __attribute__((always_inline)) {
+    const int i = i0 + (q / SV) * kFinWaves;
+    return i < ns ? (s_list[i] * SV + q % SV) * kWave + lane : nvec;
+  };
+  int nc = 0;
+  // The next step's vectors, in flight while the current step is worked.
+  CH n0, n1, n2, n3, n4, n5, n6, n7;
+  static_assert(kFinVecs == 8, "eight staged vectors");
+  auto load_step = [&](int i0) __attribute__((always_inline)) {
+    n0.load(row + (int64_t)min(vec_of(i0, 0), nvec - 1) * VEC);
+    n1.load(row + (int64_t)min(vec_of(i0, 1), nvec - 1) * VEC);
+    n2.load(row + (int64_t)min(vec_of(i0, 2), nvec - 1) * VEC);
+    n3.load(row + (int64_t)min(vec_of(i0, 3), nvec - 1) * VEC);
+    n4.load(row + (int64_t)min(vec_of(i0, 4), nvec - 1) * VEC);
+    n5.load(row + (int64_t)min(vec_of(i0, 5), nvec - 1) * VEC);
+    n6.load(row + (int64_t)min(vec_of(i0, 6), nvec - 1) * VEC);
+    n7.load(row + (int64_t)min(vec_of(i0, 7), nvec - 1) * VEC);
+  };
+  if (wave < ns) load_step(wave);
+  for (int i0 = wave; i0 < ns; i0 += NS * kFinWaves) {
+    s_stage[wave][0][lane] = n0;  // each lane reads back only its own
+    s_stage[wave][1][lane] = n1;
+    s_stage[wave][2][lane] = n2;
+    s_stage[wave][3][lane] = n3;
+    s_stage[wave][4][lane] = n4;
+    s_stage[wave][5][lane] = n5;
+    s_stage[wave][6][lane] = n6;
+    s_stage[wave][7][lane] = n7;
+    if (i0 + NS * kFinWaves < ns) load_step(i0 + NS * kFinWaves);
+    const int nq = min(NS, (ns - i0 + kFinWaves - 1) / kFinWaves) * SV;
+#pragma unroll 1
+    for (int q = 0; q < nq; ++q) {
+      const CH x = s_stage[wave][q][lane];
+      const bool ok = vec_of(i0, q) < nvec;
+      float ts = 0.0f, vmax = -INFINITY;
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float v = x.get(e);
+        const bool cnd = ok && !(v < lo);
+        cnt += cnd ? 1 : 0;
+        vmax = cnd ? fmaxf(vmax, v) : vmax;
+        if (rest_on && ok && !cnd) ts += fast_exp2((v - m) * c);
+      }
+      if (rest_on) tl += (double)ts;
+      const uint64_t any = __ballot(cnt > 0);
+      if (any == 0) continue;  // the same for every lane
+      if (__ballot(cnt > 1) == 0) {
+        if (cnt > 0) {
+          const int pos = nc + lane_rank(any);
+          if (pos < kFinCap) cand[pos] = vmax;
+        }
+        nc += (int)__popcll(any);
+      } else {
+#pragma unroll 1
+        for (int e = 0; e < VEC; ++e) {
+          const float v = x.get_dyn(e);
+          const bool cnd = ok && !(v < lo);
+          const uint64_t mk = __ballot(cnd);
+          if (cnd) {
+            const int pos = nc + lane_rank(mk);
+            if (pos < kFinCap) cand[pos] = v;
+          }
+          nc += (int)__popcll(mk);
+        }
+      }
+    }
+  }
+  const double tw = wave_sum(tl);
+  if (lane == 0) {
+    s_cnt[wave] = nc;
+    s_rest[wave] = tw;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // Wave 0: the candidates of all waves in wave order, and the rest of the row's mass.
+  nc = 0;
+  double rest = 0.0;
+  for (int w = 0; w < kFinWaves; ++w) {
+    const int cw = s_cnt[w];
+    for (int j = lane; j < cw; j += kWave)
+      if (nc + j < kFinCap) s_all[nc + j] = s_cand[w][j];
+    nc += cw;
+    rest += s_rest[w];
+  }
+  if (nc > kFinCap) {
+    done(0.0f, 1);
+    return;
+  }
+  wave_lds_sync();
+  const int nt = (nc + kWave - 1) / kWave;  // candidate slots per lane: j = t * 64 + lane
+  // top-k: the k-th largest candidate (at least k candidates reach lo), as a candidate's value.
+  float th_k = -INFINITY;
+  if (topk) {
+    if (nc < fp.k) {
+      done(0.0f, 1);
+      return;
+    }
+    const float v = bisect_key<KS>(lo, m, [&](float v) {
+      int n = 0;
+      for (int t = 0; t < nt; ++t) {
+        const int j = t * kWave + lane;
+        n += (int)__popcll(__ballot(j < nc && !(s_all[j] < v)));
+      }
+      return n >= fp.k;
+    });
+    float lowest = INFINITY;
+    for (int j = lane; j < nc; j += kWave) lowest = !(s_all[j] < v) ? fminf(lowest, s_all[j]) : lowest;
+    th_k = -wave_max(-lowest);
+  }
+  // top-p over top-k's set (the candidates >= th_k; all of them with top-p alone), S1 being
+  // the set's fp64 mass plus, with top-p alone, the rest of the row's.
+  float th_p = -INFINITY;
+  if (topp) {
+    const float base = topk ? th_k : lo;
+    double own = 0.0;
+    for (int j = lane; j < nc; j += kWave) {
+      const double e = !(s_all[j] < base) ? exp(((double)s_all[j] - (double)m) / Td) : 0.0;
+      s_e[j] = e;
+      own += e;
+    }
+    const double target = (double)fp.top_p * (wave_sum(own) + (topk ? 0.0 : rest));
+    wave_lds_sync();
+    float best = -INFINITY;
+    for (int t = 0; t < nt; ++t) {
+      const int i = t * kWave + lane;
+      const float xi = i < nc ? s_all[i] : INFINITY;
+      double h = 0.0;
+#pragma unroll 4
+      for (int j = 0; j < nc; ++j) h += !(s_all[j] < xi) ? s_e[j] : 0.0;
+      if (i < nc && !(xi < base) && h >= target) best = fmaxf(best, xi);
+    }
+    th_p = wave_max(best);
+    if (th_p == -INFINITY) {  // the candidates hold less than top_p of S1
+      done(0.0f, 1);
+      return;
+    }
+  }
+  done(fmaxf(fmaxf(th_k, th_p), th_m), 0);
+}
+
 // ====================================================================== launch
 
 // Zero the request tickets. Every ticket wraps back to zero when a call completes, so this
@@ -2588,7 +3018,7 @@ __global__ __launch_bounds__(kBlock) void clear_counters_kernel(uint32_t* t, int
 struct LayoutSeen {
   int device;
   const void* ws;
-  size_t off_ticket2, total;
+  size_t off_ticket2, off_trans;  // the counters' extent
 };
 
 static std::mutex g_layout_mu;
@@ -2605,15 +3035,15 @@ static hipError_t counters_ready(const Plan& p, char* ws, hipStream_t stream) {
   int slot = -1;
   for (int i = 0; i < g_layout_n; ++i)
     if (g_layout[i].device == dev && g_layout[i].ws == ws) slot = i;
-  if (slot >= 0 && g_layout[slot].off_ticket2 == p.off_ticket2 && g_layout[slot].total == p.total)
+  if (slot >= 0 && g_layout[slot].off_ticket2 == p.off_ticket2 && g_layout[slot].off_trans == p.off_trans)
     return hipSuccess;
-  const int64_t n = (int64_t)(p.total - p.off_ticket2) / 4;  // the ticket array sits at the end
+  const int64_t n = (int64_t)(p.off_trans - p.off_ticket2) / 4;
   const int64_t blocks = (n + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(kBlock), 0,
                      stream, reinterpret_cast<uint32_t*>(ws + p.off_ticket2), n);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (slot < 0) slot = g_layout_n < 64 ? g_layout_n++ : (int)(reinterpret_cast<uintptr_t>(ws) / 256 % 64);
-  g_layout[slot] = LayoutSeen{dev, ws, p.off_ticket2, p.total};
+  g_layout[slot] = LayoutSeen{dev, ws, p.off_ticket2, p.off_trans};
   return hipSuccess;
 }
 
@@ -2653,8 +3083,31 @@ static hipError_t resident_waves(const void* fn, int per_cu_target, int64_t* slo
 // The filtered verify's first kernel: every row's keep-thresholds, one workgroup per row
 // and side.
 template <typename E, int VEC>
-hipError_t launch_thresholds(const Plan& p, const Inputs& in, const FilterArgs& fa, hipStream_t stream) {
-  hipLaunchKernelGGL((thresholds_kernel<E, VEC>), dim3((unsigned)p.R, 2u), dim3(kFiltBlock), 0, stream, in, fa);
+hipError_t launch_thresholds(const Plan& p, const Inputs& in, FilterArgs fa, hipStream_t stream, char* ws) {
+  if constexpr (VEC > 1) {
+    if (p.nseg > 0 && ws != nullptr) {
+      fa.seg = reinterpret_cast<SegRec*>(ws + p.off_seg);
+      fa.fb = reinterpret_cast<int32_t*>(ws + p.off_fb);
+      fa.nseg = p.nseg;
+      // Waves per row and side: about forty per compute unit in all, each streaming at least
+      // 16 segments (16 KB of bf16).
+      const int64_t want = (kRecordWaves + 2 * (int64_t)p.R - 1) / (2 * (int64_t)p.R);
+      const int64_t most = p.nseg / 16 < 1 ? 1 : p.nseg / 16;
+      const int nw = (int)(want < 1 ? 1 : want > most ? most : want);
+      const int64_t blocks1 = ((int64_t)p.R * 2 * nw + kWavesPerBlock - 1) / kWavesPerBlock;
+      hipLaunchKernelGGL((seg_records_kernel<E, VEC>), dim3((unsigned)blocks1), dim3(kBlock), 0, stream, in, fa, nw);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((thresholds_finish_kernel<E, VEC>), dim3((unsigned)(2 * p.R)), dim3(kFinWaves * kWave), 0, stream,
+                         in, fa);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      // The rows and sides sent back (a few, as a rule), taken in turn by a smaller grid.
+      const unsigned blocks3 = (unsigned)(2 * (int64_t)p.R < 128 ? 2 * p.R : 128);
+      hipLaunchKernelGGL((thresholds_kernel<E, VEC, true>), dim3(blocks3), dim3(kFiltBlock), 0, stream, in, fa);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((thresholds_kernel<E, VEC, false>), dim3((unsigned)(2 * p.R)), dim3(kFiltBlock), 0, stream, in, fa);
   return hipGetLastError();
 }
 
@@ -2800,12 +3253,12 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
     in.filt[1] = fd;
     const FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
     if (p.dtype == SV_BF16) {
-      err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
+      err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream, ws) : launch_thresholds<uint16_t, 1>(p, in, fa, stream, ws);
       if (err == hipSuccess)
         err = aligned ? launch_pair<uint16_t, 8, true>(p, in, w, out, stream, ev)
                       : launch_pair<uint16_t, 1, true>(p, in, w, out, stream, ev);
     } else {
-      err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+      err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream, ws) : launch_thresholds<float, 1>(p, in, fa, stream, ws);
       if (err == hipSuccess)
         err = aligned ? launch_pair<float, 4, true>(p, in, w, out, stream, ev)
                       : launch_pair<float, 1, true>(p, in, w, out, stream, ev);
@@ -2947,12 +3400,12 @@ static sv_status row_sums_run(const void* target_logits, const void* draft_logit
     in.filt[1] = fd;
     const FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
     if (p.dtype == SV_BF16) {
-      err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
+      err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream, ws) : launch_thresholds<uint16_t, 1>(p, in, fa, stream, ws);
       if (err == hipSuccess)
         err = aligned ? launch_sums<uint16_t, 8, true>(p, in, w, out_sum_min, out_sum_pq, stream)
                       : launch_sums<uint16_t, 1, true>(p, in, w, out_sum_min, out_sum_pq, stream);
     } else {
-      err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+      err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream, ws) : launch_thresholds<float, 1>(p, in, fa, stream, ws);
       if (err == hipSuccess)
         err = aligned ? launch_sums<float, 4, true>(p, in, w, out_sum_min, out_sum_pq, stream)
                       : launch_sums<float, 1, true>(p, in, w, out_sum_min, out_sum_pq, stream);
@@ -3034,14 +3487,15 @@ extern "C" sv_status sv_filter_thresholds(const void* target_logits, const void*
   Inputs in{target_logits, draft_logits, nullptr, row_offsets, temperature, nullptr, nullptr, nullptr,
             0, p.B, p.R, p.V, p.dtype, 1, 1};
   const FilterArgs fa{{side_of(target_filter), side_of(draft_filter)}, out_theta};
+  char* ws = static_cast<char*>(workspace);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const bool aligned = ((int64_t)p.V * p.esize) % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(draft_logits) % 16) == 0;
   hipError_t err;
   if (p.dtype == SV_BF16)
-    err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream) : launch_thresholds<uint16_t, 1>(p, in, fa, stream);
+    err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream, ws) : launch_thresholds<uint16_t, 1>(p, in, fa, stream, ws);
   else
-    err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream) : launch_thresholds<float, 1>(p, in, fa, stream);
+    err = aligned ? launch_thresholds<float, 4>(p, in, fa, stream, ws) : launch_thresholds<float, 1>(p, in, fa, stream, ws);
   return err == hipSuccess ? SV_OK : SV_E_HIP;
 }
 

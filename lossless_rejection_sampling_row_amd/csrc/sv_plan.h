@@ -91,12 +91,27 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 
+// The filter chain's segment records: a segment is kSegLogits consecutive logits of a row
+// read with 16-byte vectors. Rows of more than kSegCap segments keep none.
+constexpr int kSegLogits = 512;
+constexpr int kSegCap = 512;
+struct alignas(8) SegRec {
+  float max;   // the segment's largest logit; +inf when it holds NaN or +inf
+  float mass;  // with top-p alone: sum of exp2((l - max) * c) over the segment
+};
+static_assert(sizeof(SegRec) == 8, "SegRec layout");
+
 struct Plan {
   int32_t B, R, V, dtype;
   int32_t esize;  // bytes per logit
   int32_t w1max;  // pass 1: most waves that share one row (sizes the partial array)
   int32_t w2max;  // pass 2: most waves that share one request
-  size_t off_hdr, off_part1, off_part2, off_part3, off_lazy, off_theta, off_ticket2, off_bmax, off_done3, total;
+  int32_t nseg;   // record segments per row and side (0: more than kSegCap)
+  // Persistent: the header, lazy stop flags, keep-thresholds, then the counters every call
+  // leaves at zero, [off_ticket2, off_trans). Per call, from off_trans: the partial records
+  // (off_part1..3) or, in the filter chain, the segment records and fallback flags.
+  size_t off_hdr, off_lazy, off_theta, off_ticket2, off_bmax, off_done3, off_trans;
+  size_t off_part1, off_part2, off_part3, off_seg, off_fb, total;
 };
 
 // Build the plan for a shape. Returns SV_OK, or the status describing why the

@@ -68,8 +68,6 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   q.nseg = nseg <= kSegCap ? (int32_t)nseg : 0;
   q.off_seg = off = q.off_trans;
   off += (size_t)q.R * 2 * q.nseg * sizeof(SegRec);
-  q.off_fb = off = align_up(off, 256);
-  off += (size_t)q.R * 2 * sizeof(int32_t);
   off = off > end_parts ? off : end_parts;
   q.total = align_up(off, 256);
   *p = q;

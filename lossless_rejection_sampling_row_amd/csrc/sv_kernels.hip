@@ -57,11 +57,8 @@ struct FilterSide {
 struct FilterArgs {
   FilterSide side[2];  // target, draft
   float* theta;        // [R][2] keep-thresholds, written by thresholds_kernel
-  // With segment records (16-byte rows of at most kSegCap segments): the records, [R][2][nseg],
-  // and per row and side a flag that sends it to thresholds_kernel (1) or not (0). Without
-  // (fb null), thresholds_kernel handles every row and side.
+  // With segment records (16-byte rows of at most kSegCap segments): the records, [R][2][nseg].
   SegRec* seg = nullptr;
-  int32_t* fb = nullptr;
   int32_t nseg = 0;
 };
 
@@ -2369,21 +2366,11 @@ __device__ __forceinline__ void thresholds_row(const Inputs& in, const FilterArg
   if (threadIdx.x == 0) *out = fmaxf(fmaxf(th_k, th_p), th_m);
 }
 
-// Without segment records (SENT false): workgroup i takes row i / 2, side i % 2. After the
-// record kernels (SENT true): a smaller grid takes, in turn, the rows and sides they sent
-// back (fb set).
-template <typename E, int VEC, bool SENT>
-__global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(SENT ? 4 : 6))) void thresholds_kernel(Inputs in, FilterArgs fa) {
+// Workgroup i takes row i / 2, side i % 2.
+template <typename E, int VEC>
+__global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6))) void thresholds_kernel(Inputs in, FilterArgs fa) {
   __shared__ FilterSmem s;
-  if (!SENT) {
-    thresholds_row<E, VEC>(in, fa, (int)(blockIdx.x >> 1), (int)(blockIdx.x & 1), s);
-    return;
-  }
-  for (int rs = blockIdx.x; rs < 2 * in.R; rs += gridDim.x) {
-    if (fa.fb[rs] == 0) continue;  // the same for the whole workgroup
-    thresholds_row<E, VEC>(in, fa, rs >> 1, rs & 1, s);
-    __syncthreads();  // the next row reuses s
-  }
+  thresholds_row<E, VEC>(in, fa, (int)(blockIdx.x >> 1), (int)(blockIdx.x & 1), s);
 }
 
 // ====================================================================== sampler-match rule
@@ -2697,15 +2684,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 constexpr int kRecordWaves = 10240;  // seg_records_kernel's target grid, in waves
-constexpr int kFinWaves = 4;         // waves per row and side in thresholds_finish_kernel
-constexpr int kFinCap = 256;         // candidates a row and side keeps
-constexpr int kFinVecs = 8;          // 16-byte vectors per lane one gather step stages
+constexpr int kFinWaves = kFiltWaves;  // waves per row and side in thresholds_finish_kernel
+constexpr int kFinCap = 256;           // candidates a row and side keeps
+constexpr int kFinVecs = 8;            // 16-byte vectors per lane one gather step loads
+constexpr int kFinStage = 4;           // of which the LDS stage holds this many at a time
 
 // Largest v in [lo, hi] with pred(v), pred monotone (true below some point, false above) and
 // true at lo, found by bisection over order_key(v) / 2^S: with bf16 data (S = 16) every probe
 // lies just below or on a bf16 value, so {x >= v} over the data is decided in 16 steps.
 template <int S, class P>
-__device__ float bisect_key(float lo, float hi, P pred) {
+__device__ __forceinline__ float bisect_key(float lo, float hi, P pred) {
   if (pred(hi)) return hi;
   int64_t a = (int64_t)(order_key(lo) >> S), z = (int64_t)(order_key(hi) >> S) + 1;
   while (z - a > 1) {
@@ -2716,188 +2704,188 @@ __device__ float bisect_key(float lo, float hi, P pred) {
   return key_float((int32_t)(a * ((int64_t)1 << S)));
 }
 
-// kFinWaves waves per row and side (grid 2R). The kernel runs once per row and side, so its
-// instructions come cold from L2: the code keeps to short loops. Every wave keeps the
-// records of segments lane, lane + 64, ... in registers and takes the same decisions up to
-// the gather; the gather splits the listed segments over the waves (loads staged in LDS,
-// then one vector per loop step); wave 0 then decides the thresholds alone. Selections by
-// value are bisections over the float order (bisect_key) whose steps count with ballots: the
-// k-th largest value is the largest v that at least k values reach. top-p's threshold is the
-// largest candidate x whose candidates >= x hold at least top_p times S1: every lane sums,
-// for its own candidates, the masses of all candidates at or above them.
 template <typename E, int VEC>
-__global__ __launch_bounds__(kFinWaves * kWave) void thresholds_finish_kernel(Inputs in, FilterArgs fa) {
+struct FinSmem {
+  int list[kSegCap];                                 // the segments to gather, in row order
+  Chunk<E, VEC> stage[kFinWaves][kFinStage][kWave];  // each lane's staged vectors
+  float cand[kFinWaves][kFinCap];                    // each wave's candidates, in gather order
+  float all[kFinCap];                                // all of them, wave 0's first
+  double e[kFinCap];                                 // masses exp((x - m) / T), 0 below the base
+  int cnt[kFinWaves];
+  double rest[kFinWaves];
+  float th, lo, m;
+  int ns, mode, back;
+};
+
+// One workgroup of kFiltBlock threads per row and side (grid 2R). It runs once per row and
+// side, latency-bound, so the code keeps to short loops. Every wave keeps the records of
+// segments lane, lane + 64, ... in registers and takes the same decisions up to the gather;
+// the gather splits the listed segments over the waves (loads staged through LDS); wave 0
+// then decides the thresholds alone. Selections by value are bisections over the float order
+// (bisect_key) whose steps count with ballots: the k-th largest value is the largest v that
+// at least k values reach. top-p's threshold is the largest candidate x whose candidates >= x
+// hold at least top_p times S1: every lane sums, for its own candidates, the masses of all
+// candidates at or above them. A row and side that the records cannot decide (top-k beyond
+// the segment count, more than kFinCap candidates, candidates short of top_p) is decided by
+// the whole workgroup as thresholds_kernel does, in the same LDS.
+template <typename E, int VEC>
+__global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6))) void thresholds_finish_kernel(Inputs in, FilterArgs fa) {
   using CH = Chunk<E, VEC>;
   constexpr int RS = kSegCap / kWave;  // record slots per lane
   constexpr int KS = sizeof(E) == 2 ? 16 : 0;  // bisection granularity: bf16 values
   constexpr int SV = kSegLogits / (kWave * VEC);
   constexpr int NS = kFinVecs / SV;  // listed segments per wave and gather step
-  __shared__ int s_list[kSegCap];               // the segments to gather, in row order
-  __shared__ CH s_stage[kFinWaves][kFinVecs][kWave];
-  __shared__ float s_cand[kFinWaves][kFinCap];  // each wave's candidates, in gather order
-  __shared__ float s_all[kFinCap];              // all of them, wave 0's first
-  __shared__ double s_e[kFinCap];               // masses exp((x - m) / T), 0 below the base
-  __shared__ int s_cnt[kFinWaves];
-  __shared__ double s_rest[kFinWaves];
+  __shared__ union {
+    FinSmem<E, VEC> f;
+    FilterSmem x;
+  } u;
+  FinSmem<E, VEC>& F = u.f;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int rs = blockIdx.x, r = rs >> 1, side = rs & 1;
   float* out = fa.theta + rs;  // theta is [R][2]
-  int32_t* fb = fa.fb + rs;
   const int b = uni(request_of_row(in, r));
   const float T = in.temp[b];
   const FilterParams fp = filter_params(fa.side[side], b);
   const bool topk = fp.k > 0 && fp.k < in.V, topp = fp.top_p < 1.0f, minp = fp.min_p > 0.0f;
-  // Every exit before the gather is taken by the whole workgroup alike.
-  auto done = [&](float th, int back) __attribute__((always_inline)) {
-    if (threadIdx.x == 0) {
-      if (!back) *out = th;
-      *fb = back;
-    }
+  auto done = [&](float th) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) *out = th;
   };
   if (!(T > 0.0f) || !temperature_ok(T) || !filter_valid(fp) || !(topk || topp || minp)) {
-    done(-INFINITY, 0);
+    done(-INFINITY);
     return;
   }
   const int nseg = fa.nseg;
-  if (topk && fp.k > nseg) {
-    done(0.0f, 1);
-    return;
-  }
+  if (!(topk && fp.k > nseg)) {  // else the exact path below
   const bool rest_on = topp && !topk;  // top-p alone: S1 is the whole row's mass
-  const SegRec* rec = fa.seg + (int64_t)rs * nseg;
-  float smax[RS], smass[RS];
-  float mx = -INFINITY;
-  int bad = 0;
-#pragma unroll
-  for (int t = 0; t < RS; ++t) {
-    smax[t] = -INFINITY;
-    smass[t] = 0.0f;
-    if (t * kWave + lane < nseg) {
-      const SegRec q = rec[t * kWave + lane];
-      smax[t] = q.max;
-      smass[t] = q.mass;
-    }
-    bad |= (int)!(smax[t] < INFINITY);
-    mx = fmaxf(mx, smax[t]);
-  }
-  const float m = wave_max(mx);
-  if (wave_or(bad) != 0 || m == -INFINITY) {
-    done(INFINITY, 0);
-    return;
-  }
   const double Td = (double)T;
-  // min-p: the smallest float y with (y - m) / T >= ln(min_p), in fp64 (as thresholds_kernel).
-  float th_m = -INFINITY;
-  if (minp) {
-    const double lm = log((double)fp.min_p);
-    auto keep = [&](float y) { return ((double)y - (double)m) / Td >= lm; };
-    float y = (float)((double)m + Td * lm);
-    for (int it = 0; it < 64 && !keep(y); ++it) y = nextafterf(y, INFINITY);
-    for (int it = 0; it < 64 && keep(nextafterf(y, -INFINITY)); ++it) y = nextafterf(y, -INFINITY);
-    th_m = y;
-  }
-  if (!topk && !topp) {
-    done(th_m, 0);
-    return;
-  }
   const float c = scale_of(T);
-  // The candidate bound lo: every logit at or above the threshold to find reaches it.
-  //  - top-k: the k-th largest segment maximum (k segments hold a logit that reaches it).
-  //  - top-p alone: start from the window bound (as thresholds_kernel), then raise it to the
-  //    largest v at which the records still prove that the logits >= v hold top_p of the
-  //    row's mass: those in segments whose maximum reaches v hold at least their segments'
-  //    mass less kSegLogits * exp((v - m) / T) per segment. The records' masses are fp32
-  //    sums, so the proof keeps a margin of 2e-4 of the row's mass; the top-p search below
-  //    still checks that the candidates reach top_p.
-  float f[RS];  // top-p alone: exp2((segment max - m) * c), each segment's scale to m
-  float lo;
-  if (topk) {
-    lo = bisect_key<KS>(-INFINITY, m, [&](float v) {
-      int n = 0;
-#pragma unroll
-      for (int t = 0; t < RS; ++t) n += (int)__popcll(__ballot(!(smax[t] < v)));
-      return n >= fp.k;
-    });
-  } else {
-    float Mf[RS];
-    double S = 0.0;
+  float th_m = -INFINITY;  // min-p's threshold (wave 0's)
+  double tl = 0.0;         // with top-p alone, this wave's share of the mass outside the candidates
+  // Wave 0 alone reads the records and decides up to the list of segments to gather; the other
+  // waves wait. mode 0: the threshold is decided (th); 1: gather the logits >= lo.
+  if (wave == 0) {
+    const SegRec* rec = fa.seg + (int64_t)rs * nseg;
+    float smax[RS], smass[RS];
+    float mx = -INFINITY;
+    int bad = 0;
 #pragma unroll
     for (int t = 0; t < RS; ++t) {
-      f[t] = smax[t] > -INFINITY ? fast_exp2((smax[t] - m) * c) : 0.0f;
-      Mf[t] = smass[t] * f[t];
-      S += (double)smass[t] * (double)f[t];
-    }
-    S = wave_sum(S);
-    const float W = log2f((float)in.V / (1.0f - fp.top_p)) + 1.0f;
-    const double need = (double)fp.top_p * S + 2e-4 * S;
-    lo = bisect_key<KS>(m - (W + 0.01f) / c, m, [&](float v) {
-      float h = 0.0f;
-      int n = 0;
-#pragma unroll
-      for (int t = 0; t < RS; ++t) {
-        const bool on = !(smax[t] < v);
-        h += on ? Mf[t] : 0.0f;
-        n += (int)__popcll(__ballot(on));
+      smax[t] = -INFINITY;
+      smass[t] = 0.0f;
+      if (t * kWave + lane < nseg) {
+        const SegRec q = rec[t * kWave + lane];
+        smax[t] = q.max;
+        smass[t] = q.mass;
       }
-      const double held = (double)wave_sum(h);
-      return held - (double)n * (double)kSegLogits * exp(((double)v - (double)m) / Td) >= need;
-    });
-  }
-  // The segments that can hold candidates, in row order (listed by wave 0); with top-p alone
-  // the others' mass (summed by wave 0).
-  double tl = 0.0;
-  int ns = 0;
+      bad |= (int)!(smax[t] < INFINITY);
+      mx = fmaxf(mx, smax[t]);
+    }
+    const float m = wave_max(mx);
+    int mode = 1, ns = 0;
+    float th = 0.0f, lo = 0.0f;
+    if (wave_or(bad) != 0 || m == -INFINITY) {
+      mode = 0;
+      th = INFINITY;
+    } else {
+      // min-p: the smallest float y with (y - m) / T >= ln(min_p), in fp64 (as
+      // thresholds_kernel).
+      if (minp) {
+        const double lm = log((double)fp.min_p);
+        auto keep = [&](float y) { return ((double)y - (double)m) / Td >= lm; };
+        float y = (float)((double)m + Td * lm);
+        for (int it = 0; it < 64 && !keep(y); ++it) y = nextafterf(y, INFINITY);
+        for (int it = 0; it < 64 && keep(nextafterf(y, -INFINITY)); ++it) y = nextafterf(y, -INFINITY);
+        th_m = y;
+      }
+      if (!topk && !topp) {
+        mode = 0;
+        th = th_m;
+      } else {
+        // The candidate bound lo: every logit at or above the threshold to find reaches it.
+        //  - top-k: the k-th largest segment maximum (k segments hold a logit that reaches it).
+        //  - top-p alone: start from the window bound (as thresholds_kernel), then raise it to
+        //    the largest v at which the records still prove that the logits >= v hold top_p of
+        //    the row's mass: those in segments whose maximum reaches v hold at least their
+        //    segments' mass less kSegLogits * exp((v - m) / T) per segment. The records'
+        //    masses are fp32 sums, so the proof keeps a margin of 2e-4 of the row's mass; the
+        //    top-p search below still checks that the candidates reach top_p.
+        if (topk) {
+          lo = bisect_key<KS>(-INFINITY, m, [&](float v) {
+            int n = 0;
 #pragma unroll
-  for (int t = 0; t < RS; ++t) {
-    const bool real = t * kWave + lane < nseg;
-    const bool take = real && !(smax[t] < lo);
-    if (wave == 0 && rest_on && real && !take) tl += (double)smass[t] * (double)f[t];
-    const uint64_t mk = __ballot(take);
-    if (wave == 0 && take) s_list[ns + lane_rank(mk)] = t * kWave + lane;
-    ns += (int)__popcll(mk);
+            for (int t = 0; t < RS; ++t) n += (int)__popcll(__ballot(!(smax[t] < v)));
+            return n >= fp.k;
+          });
+        } else {
+          // From here on smass holds each segment's mass relative to m.
+          double S = 0.0;
+#pragma unroll
+          for (int t = 0; t < RS; ++t) {
+            smass[t] = smax[t] > -INFINITY ? smass[t] * fast_exp2((smax[t] - m) * c) : 0.0f;
+            S += (double)smass[t];
+          }
+          S = wave_sum(S);
+          const float W = log2f((float)in.V / (1.0f - fp.top_p)) + 1.0f;
+          const double need = (double)fp.top_p * S + 2e-4 * S;
+          lo = bisect_key<KS>(m - (W + 0.01f) / c, m, [&](float v) {
+            float h = 0.0f;
+            int n = 0;
+#pragma unroll
+            for (int t = 0; t < RS; ++t) {
+              const bool on = !(smax[t] < v);
+              h += on ? smass[t] : 0.0f;
+              n += (int)__popcll(__ballot(on));
+            }
+            const double held = (double)wave_sum(h);
+            return held - (double)n * (double)kSegLogits * exp(((double)v - (double)m) / Td) >= need;
+          });
+        }
+        // The segments that can hold candidates, in row order; with top-p alone the others'
+        // mass.
+#pragma unroll
+        for (int t = 0; t < RS; ++t) {
+          const bool real = t * kWave + lane < nseg;
+          const bool take = real && !(smax[t] < lo);
+          if (rest_on && real && !take) tl += (double)smass[t];
+          const uint64_t mk = __ballot(take);
+          if (take) F.list[ns + lane_rank(mk)] = t * kWave + lane;
+          ns += (int)__popcll(mk);
+        }
+      }
+    }
+    if (lane == 0) {
+      F.mode = mode;
+      F.th = th;
+      F.lo = lo;
+      F.m = m;
+      F.ns = ns;
+    }
   }
   __syncthreads();
+  if (F.mode == 0) {
+    done(F.th);
+    return;
+  }
+  const float lo = F.lo, m = F.m;
+  const int ns = F.ns;
   // Gather the logits >= lo: wave w takes listed segments w, w + kFinWaves, ..., NS at a
-  // time. A vector whose lanes hold at most one candidate each stores each lane's largest
-  // logit at the lane's rank; otherwise one ballot per element.
+  // time, kFinVecs vectors per lane loaded at once and worked through the LDS stage
+  // kFinStage at a time. A vector whose lanes hold at most one candidate each stores each
+  // lane's largest logit at the lane's rank; otherwise one ballot per element.
   const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
   const int nvec = in.V / VEC;
-  float* cand = s_cand[wave];
+  float* cand = F.cand[wave];
   auto vec_of = [&](int i0, int q) __attribute__((always_inline)) {
     const int i = i0 + (q / SV) * kFinWaves;
-    return i < ns ? (s_list[i] * SV + q % SV) * kWave + lane : nvec;
+    return i < ns ? (F.list[i] * SV + q % SV) * kWave + lane : nvec;
   };
   int nc = 0;
-  // The next step's vectors, in flight while the current step is worked.
-  CH n0, n1, n2, n3, n4, n5, n6, n7;
-  static_assert(kFinVecs == 8, "eight staged vectors");
-  auto load_step = [&](int i0) __attribute__((always_inline)) {
-    n0.load(row + (int64_t)min(vec_of(i0, 0), nvec - 1) * VEC);
-    n1.load(row + (int64_t)min(vec_of(i0, 1), nvec - 1) * VEC);
-    n2.load(row + (int64_t)min(vec_of(i0, 2), nvec - 1) * VEC);
-    n3.load(row + (int64_t)min(vec_of(i0, 3), nvec - 1) * VEC);
-    n4.load(row + (int64_t)min(vec_of(i0, 4), nvec - 1) * VEC);
-    n5.load(row + (int64_t)min(vec_of(i0, 5), nvec - 1) * VEC);
-    n6.load(row + (int64_t)min(vec_of(i0, 6), nvec - 1) * VEC);
-    n7.load(row + (int64_t)min(vec_of(i0, 7), nvec - 1) * VEC);
-  };
-  if (wave < ns) load_step(wave);
-  for (int i0 = wave; i0 < ns; i0 += NS * kFinWaves) {
-    s_stage[wave][0][lane] = n0;  // each lane reads back only its own
-    s_stage[wave][1][lane] = n1;
-    s_stage[wave][2][lane] = n2;
-    s_stage[wave][3][lane] = n3;
-    s_stage[wave][4][lane] = n4;
-    s_stage[wave][5][lane] = n5;
-    s_stage[wave][6][lane] = n6;
-    s_stage[wave][7][lane] = n7;
-    if (i0 + NS * kFinWaves < ns) load_step(i0 + NS * kFinWaves);
-    const int nq = min(NS, (ns - i0 + kFinWaves - 1) / kFinWaves) * SV;
+  auto work = [&](int i0, int q0, int nq) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int q = 0; q < nq; ++q) {
-      const CH x = s_stage[wave][q][lane];
-      const bool ok = vec_of(i0, q) < nvec;
+      const CH x = F.stage[wave][q][lane];
+      const bool ok = vec_of(i0, q0 + q) < nvec;
       float ts = 0.0f, vmax = -INFINITY;
       int cnt = 0;
 #pragma unroll
@@ -2931,78 +2919,104 @@ __global__ __launch_bounds__(kFinWaves * kWave) void thresholds_finish_kernel(In
         }
       }
     }
+  };
+  static_assert(kFinVecs == 2 * kFinStage, "two stage fills per step");
+  for (int i0 = wave; i0 < ns; i0 += NS * kFinWaves) {
+    CH x[kFinVecs];
+#pragma unroll
+    for (int q = 0; q < kFinVecs; ++q) x[q].load(row + (int64_t)min(vec_of(i0, q), nvec - 1) * VEC);
+    const int nv = min(NS, (ns - i0 + kFinWaves - 1) / kFinWaves) * SV;  // vectors of this step
+#pragma unroll
+    for (int q = 0; q < kFinStage; ++q) F.stage[wave][q][lane] = x[q];  // each lane reads back its own
+    work(i0, 0, min(nv, kFinStage));
+    if (nv > kFinStage) {
+#pragma unroll
+      for (int q = 0; q < kFinStage; ++q) F.stage[wave][q][lane] = x[kFinStage + q];
+      work(i0, kFinStage, nv - kFinStage);
+    }
   }
   const double tw = wave_sum(tl);
   if (lane == 0) {
-    s_cnt[wave] = nc;
-    s_rest[wave] = tw;
+    F.cnt[wave] = nc;
+    F.rest[wave] = tw;
   }
   __syncthreads();
-  if (wave != 0) return;
-  // Wave 0: the candidates of all waves in wave order, and the rest of the row's mass.
-  nc = 0;
-  double rest = 0.0;
-  for (int w = 0; w < kFinWaves; ++w) {
-    const int cw = s_cnt[w];
-    for (int j = lane; j < cw; j += kWave)
-      if (nc + j < kFinCap) s_all[nc + j] = s_cand[w][j];
-    nc += cw;
-    rest += s_rest[w];
+  if (wave == 0) {
+    // Wave 0: the candidates of all waves in wave order, the rest of the row's mass, then the
+    // thresholds; back = 1 hands the row to the exact path below.
+    int back = 1;
+    float th = 0.0f;
+    do {
+      int n = 0;
+      double rest = 0.0;
+      for (int w = 0; w < kFinWaves; ++w) {
+        const int cw = F.cnt[w];
+        for (int j = lane; j < cw; j += kWave)
+          if (n + j < kFinCap) F.all[n + j] = F.cand[w][j];
+        n += cw;
+        rest += F.rest[w];
+      }
+      if (n > kFinCap) break;
+      wave_lds_sync();
+      const int nt = (n + kWave - 1) / kWave;  // candidate slots per lane: j = t * 64 + lane
+      // top-k: the k-th largest candidate (at least k candidates reach lo), as a candidate's
+      // value.
+      float th_k = -INFINITY;
+      if (topk) {
+        if (n < fp.k) break;
+        const float v = bisect_key<KS>(lo, m, [&](float v) {
+          int cnt = 0;
+          for (int t = 0; t < nt; ++t) {
+            const int j = t * kWave + lane;
+            cnt += (int)__popcll(__ballot(j < n && !(F.all[j] < v)));
+          }
+          return cnt >= fp.k;
+        });
+        float lowest = INFINITY;
+        for (int j = lane; j < n; j += kWave) lowest = !(F.all[j] < v) ? fminf(lowest, F.all[j]) : lowest;
+        th_k = -wave_max(-lowest);
+      }
+      // top-p over top-k's set (the candidates >= th_k; all of them with top-p alone), S1
+      // being the set's fp64 mass plus, with top-p alone, the rest of the row's.
+      float th_p = -INFINITY;
+      if (topp) {
+        const float base = topk ? th_k : lo;
+        double own = 0.0;
+        for (int j = lane; j < n; j += kWave) {
+          const double e = !(F.all[j] < base) ? exp(((double)F.all[j] - (double)m) / Td) : 0.0;
+          F.e[j] = e;
+          own += e;
+        }
+        const double target = (double)fp.top_p * (wave_sum(own) + (topk ? 0.0 : rest));
+        wave_lds_sync();
+        float best = -INFINITY;
+        for (int t = 0; t < nt; ++t) {
+          const int i = t * kWave + lane;
+          const float xi = i < n ? F.all[i] : INFINITY;
+          double h = 0.0;
+#pragma unroll 4
+          for (int j = 0; j < n; ++j) h += !(F.all[j] < xi) ? F.e[j] : 0.0;
+          if (i < n && !(xi < base) && h >= target) best = fmaxf(best, xi);
+        }
+        th_p = wave_max(best);
+        if (th_p == -INFINITY) break;  // the candidates hold less than top_p of S1
+      }
+      th = fmaxf(fmaxf(th_k, th_p), th_m);
+      back = 0;
+    } while (false);
+    if (lane == 0) {
+      F.th = th;
+      F.back = back;
+    }
   }
-  if (nc > kFinCap) {
-    done(0.0f, 1);
+  __syncthreads();
+  if (F.back == 0) {
+    done(F.th);
     return;
   }
-  wave_lds_sync();
-  const int nt = (nc + kWave - 1) / kWave;  // candidate slots per lane: j = t * 64 + lane
-  // top-k: the k-th largest candidate (at least k candidates reach lo), as a candidate's value.
-  float th_k = -INFINITY;
-  if (topk) {
-    if (nc < fp.k) {
-      done(0.0f, 1);
-      return;
-    }
-    const float v = bisect_key<KS>(lo, m, [&](float v) {
-      int n = 0;
-      for (int t = 0; t < nt; ++t) {
-        const int j = t * kWave + lane;
-        n += (int)__popcll(__ballot(j < nc && !(s_all[j] < v)));
-      }
-      return n >= fp.k;
-    });
-    float lowest = INFINITY;
-    for (int j = lane; j < nc; j += kWave) lowest = !(s_all[j] < v) ? fminf(lowest, s_all[j]) : lowest;
-    th_k = -wave_max(-lowest);
+  __syncthreads();  // the exact path reuses the LDS
   }
-  // top-p over top-k's set (the candidates >= th_k; all of them with top-p alone), S1 being
-  // the set's fp64 mass plus, with top-p alone, the rest of the row's.
-  float th_p = -INFINITY;
-  if (topp) {
-    const float base = topk ? th_k : lo;
-    double own = 0.0;
-    for (int j = lane; j < nc; j += kWave) {
-      const double e = !(s_all[j] < base) ? exp(((double)s_all[j] - (double)m) / Td) : 0.0;
-      s_e[j] = e;
-      own += e;
-    }
-    const double target = (double)fp.top_p * (wave_sum(own) + (topk ? 0.0 : rest));
-    wave_lds_sync();
-    float best = -INFINITY;
-    for (int t = 0; t < nt; ++t) {
-      const int i = t * kWave + lane;
-      const float xi = i < nc ? s_all[i] : INFINITY;
-      double h = 0.0;
-#pragma unroll 4
-      for (int j = 0; j < nc; ++j) h += !(s_all[j] < xi) ? s_e[j] : 0.0;
-      if (i < nc && !(xi < base) && h >= target) best = fmaxf(best, xi);
-    }
-    th_p = wave_max(best);
-    if (th_p == -INFINITY) {  // the candidates hold less than top_p of S1
-      done(0.0f, 1);
-      return;
-    }
-  }
-  done(fmaxf(fmaxf(th_k, th_p), th_m), 0);
+  thresholds_row<E, VEC>(in, fa, r, side, u.x);
 }
 
 // ====================================================================== launch
@@ -3087,7 +3101,6 @@ hipError_t launch_thresholds(const Plan& p, const Inputs& in, FilterArgs fa, hip
   if constexpr (VEC > 1) {
     if (p.nseg > 0 && ws != nullptr) {
       fa.seg = reinterpret_cast<SegRec*>(ws + p.off_seg);
-      fa.fb = reinterpret_cast<int32_t*>(ws + p.off_fb);
       fa.nseg = p.nseg;
       // Waves per row and side: about forty per compute unit in all, each streaming at least
       // 16 segments (16 KB of bf16).
@@ -3096,18 +3109,14 @@ hipError_t launch_thresholds(const Plan& p, const Inputs& in, FilterArgs fa, hip
       const int nw = (int)(want < 1 ? 1 : want > most ? most : want);
       const int64_t blocks1 = ((int64_t)p.R * 2 * nw + kWavesPerBlock - 1) / kWavesPerBlock;
       hipLaunchKernelGGL((seg_records_kernel<E, VEC>), dim3((unsigned)blocks1), dim3(kBlock), 0, stream, in, fa, nw);
-      hipError_t err = hipGetLastError();
+      const hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL((thresholds_finish_kernel<E, VEC>), dim3((unsigned)(2 * p.R)), dim3(kFinWaves * kWave), 0, stream,
+      hipLaunchKernelGGL((thresholds_finish_kernel<E, VEC>), dim3((unsigned)(2 * p.R)), dim3(kFiltBlock), 0, stream,
                          in, fa);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-      // The rows and sides sent back (a few, as a rule), taken in turn by a smaller grid.
-      const unsigned blocks3 = (unsigned)(2 * (int64_t)p.R < 128 ? 2 * p.R : 128);
-      hipLaunchKernelGGL((thresholds_kernel<E, VEC, true>), dim3(blocks3), dim3(kFiltBlock), 0, stream, in, fa);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((thresholds_kernel<E, VEC, false>), dim3((unsigned)(2 * p.R)), dim3(kFiltBlock), 0, stream, in, fa);
+  hipLaunchKernelGGL((thresholds_kernel<E, VEC>), dim3((unsigned)(2 * p.R)), dim3(kFiltBlock), 0, stream, in, fa);
   return hipGetLastError();
 }
 

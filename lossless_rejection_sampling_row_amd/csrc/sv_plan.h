@@ -109,9 +109,9 @@ struct Plan {
   int32_t nseg;   // record segments per row and side (0: more than kSegCap)
   // Persistent: the header, lazy stop flags, keep-thresholds, then the counters every call
   // leaves at zero, [off_ticket2, off_trans). Per call, from off_trans: the partial records
-  // (off_part1..3) or, in the filter chain, the segment records and fallback flags.
+  // (off_part1..3) or, earlier in the filter chain, the segment records (off_seg).
   size_t off_hdr, off_lazy, off_theta, off_ticket2, off_bmax, off_done3, off_trans;
-  size_t off_part1, off_part2, off_part3, off_seg, off_fb, total;
+  size_t off_part1, off_part2, off_part3, off_seg, total;
 };
 
 // Build the plan for a shape. Returns SV_OK, or the status describing why the

@@ -2014,9 +2014,12 @@ __device__ float bisect_float(float lo, float hi, P pred) {
   return key_float((int32_t)a);
 }
 
-// Keep-threshold of row r, side `side`, by the whole workgroup.
+// Keep-threshold of row r, side `side`, by the whole workgroup. With top-p alone, lo_hint
+// may raise the candidate bound: a value that at least top_p of the row's mass reaches (the
+// top-p scan still checks it).
 template <typename E, int VEC>
-__device__ __forceinline__ void thresholds_row(const Inputs& in, const FilterArgs& fa, int r, int side, FilterSmem& s) {
+__device__ __forceinline__ void thresholds_row(const Inputs& in, const FilterArgs& fa, int r, int side, FilterSmem& s,
+                                               float lo_hint = -INFINITY) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   float* out = fa.theta + 2 * (int64_t)r + side;
@@ -2157,7 +2160,7 @@ __device__ __forceinline__ void thresholds_row(const Inputs& in, const FilterArg
   }
   // One bound for both: the gathered logits are those >= lo. The window's bound sits a little
   // below m - W / c, so that fp32 rounding can only widen it.
-  const float lo = by_edge ? edge : m - (W + 0.01f) / c;
+  const float lo = by_edge ? edge : topk ? m - (W + 0.01f) / c : fmaxf(m - (W + 0.01f) / c, lo_hint);
   // ---- gather, sort, scan
   // gather(bound, ...): the logits >= the bound go to s.cand. Returns how many there are
   // (those past kCandCap are counted, not stored). Per step each lane counts its candidates
@@ -2624,7 +2627,7 @@ __global__ __launch_bounds__(kBlock) void seg_records_kernel(Inputs in, FilterAr
   const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
   SegRec* rec = fa.seg + (int64_t)rs * nseg;
   using CH = Chunk<E, VEC>;
-  constexpr int U = 4 / SV;  // segments per step (four vectors per lane), two steps in flight
+  constexpr int U = 2 / SV;  // segments per step (two vectors per lane), two steps in flight
   auto vec_of = [&](int sg, int v) __attribute__((always_inline)) { return (sg * SV + v) * kWave + lane; };
   auto load = [&](CH (&x)[U][SV], int sb) __attribute__((always_inline)) {
 #pragma unroll
@@ -2683,7 +2686,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-constexpr int kRecordWaves = 10240;  // seg_records_kernel's target grid, in waves
+constexpr int kRecordWaves = 8192;   // seg_records_kernel's target grid, in waves
 constexpr int kFinWaves = kFiltWaves;  // waves per row and side in thresholds_finish_kernel
 constexpr int kFinCap = 256;           // candidates a row and side keeps
 constexpr int kFinVecs = 8;            // 16-byte vectors per lane one gather step loads
@@ -2756,6 +2759,7 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
     return;
   }
   const int nseg = fa.nseg;
+  float hint = -INFINITY;  // the exact path's candidate bound with top-p alone
   if (!(topk && fp.k > nseg)) {  // else the exact path below
   const bool rest_on = topp && !topk;  // top-p alone: S1 is the whole row's mass
   const double Td = (double)T;
@@ -2990,13 +2994,19 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
         const double target = (double)fp.top_p * (wave_sum(own) + (topk ? 0.0 : rest));
         wave_lds_sync();
         float best = -INFINITY;
-        for (int t = 0; t < nt; ++t) {
-          const int i = t * kWave + lane;
-          const float xi = i < n ? F.all[i] : INFINITY;
-          double h = 0.0;
+        for (int t = 0; t < nt; t += 2) {
+          const int i0 = t * kWave + lane, i1 = i0 + kWave;
+          const float x0 = i0 < n ? F.all[i0] : INFINITY, x1 = i1 < n ? F.all[i1] : INFINITY;
+          double h0 = 0.0, h1 = 0.0;
 #pragma unroll 4
-          for (int j = 0; j < n; ++j) h += !(F.all[j] < xi) ? F.e[j] : 0.0;
-          if (i < n && !(xi < base) && h >= target) best = fmaxf(best, xi);
+          for (int j = 0; j < n; ++j) {
+            const float xj = F.all[j];
+            const double ej = F.e[j];
+            h0 += !(xj < x0) ? ej : 0.0;
+            h1 += !(xj < x1) ? ej : 0.0;
+          }
+          if (i0 < n && !(x0 < base) && h0 >= target) best = fmaxf(best, x0);
+          if (i1 < n && !(x1 < base) && h1 >= target) best = fmaxf(best, x1);
         }
         th_p = wave_max(best);
         if (th_p == -INFINITY) break;  // the candidates hold less than top_p of S1
@@ -3014,9 +3024,10 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
     done(F.th);
     return;
   }
+  if (rest_on) hint = lo;
   __syncthreads();  // the exact path reuses the LDS
   }
-  thresholds_row<E, VEC>(in, fa, r, side, u.x);
+  thresholds_row<E, VEC>(in, fa, r, side, u.x, hint);
 }
 
 // ====================================================================== launch
@@ -3102,8 +3113,8 @@ hipError_t launch_thresholds(const Plan& p, const Inputs& in, FilterArgs fa, hip
     if (p.nseg > 0 && ws != nullptr) {
       fa.seg = reinterpret_cast<SegRec*>(ws + p.off_seg);
       fa.nseg = p.nseg;
-      // Waves per row and side: about forty per compute unit in all, each streaming at least
-      // 16 segments (16 KB of bf16).
+      // Waves per row and side: about 32 per compute unit in all, each streaming at least 16
+      // segments (16 KB of bf16).
       const int64_t want = (kRecordWaves + 2 * (int64_t)p.R - 1) / (2 * (int64_t)p.R);
       const int64_t most = p.nseg / 16 < 1 ? 1 : p.nseg / 16;
       const int nw = (int)(want < 1 ? 1 : want > most ? most : want);

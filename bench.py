@@ -324,7 +324,7 @@ def bench_lazy(args, binding, torch, sets, ws, stream):
 
 
 def filtered_rows(w, filt) -> int:
-    """Rows the thresholds kernel reads on one side: every row of a request with T > 0 and an
+    """Rows the thresholds chain reads on one side: every row of a request with T > 0 and an
     active filter on that side."""
     k, tp, mp = filt
     ro = w.row_offsets.astype(np.int64)
@@ -334,8 +334,9 @@ def filtered_rows(w, filt) -> int:
 
 def bench_filtered(args, binding, torch, sets, ws, stream):
     """K filtered verify calls (top-k / top-p / min-p on both sides), and K calls of the
-    thresholds kernel alone. The thresholds kernel's algorithmic bytes are one read of every
-    row it filters; the whole call adds pass 1's and pass 2's bytes."""
+    thresholds chain alone (sv_filter_thresholds: seg_records_kernel, then
+    thresholds_finish_kernel). The chain's algorithmic bytes are one read of every row it
+    filters; the whole call adds pass 1's and pass 2's bytes."""
     from lossless_rejection_sampling_row_amd import workloads as wl
     K, W = args.steps, args.warmup
     nsets = len(sets)
@@ -388,7 +389,7 @@ def bench_filtered(args, binding, torch, sets, ws, stream):
                      for i in range(K)], dtype=np.float64)
     th_gbps = th_bytes.mean() / (ms_th / 1e3) / 1e9
     gbps = (th_bytes.mean() + pair.mean()) / (ms / 1e3) / 1e9
-    log(f"[bench] filtered verify: {ms * 1e3:.1f} us/step ({gbps:.0f} GB/s of algorithmic bytes); thresholds kernel "
+    log(f"[bench] filtered verify: {ms * 1e3:.1f} us/step ({gbps:.0f} GB/s of algorithmic bytes); thresholds chain "
         f"alone {ms_th * 1e3:.1f} us ({th_gbps:.0f} GB/s, one read of each filtered row)")
     line = {
         "metric": "verified rows/sec, filtered verify (top-k / top-p / min-p on p and q)",
@@ -408,7 +409,8 @@ def bench_filtered(args, binding, torch, sets, ws, stream):
                    "filters": "per request: top_k {0,20,50}, top_p {1,0.9,0.95}, min_p {0,0.05}, each side"},
         "thresholds_us": round(ms_th * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(th_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(th_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "thresholds_kernel",
+                     "frac": round(th_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "seg_records_kernel + thresholds_finish_kernel (one sv_filter_thresholds call)",
                      "launch_us": round(ms_th * 1e3, 2), "alg_bytes_per_launch": int(th_bytes.mean())},
         "whole_call": {"achieved": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                        "alg_bytes_per_call": int(th_bytes.mean() + pair.mean())},
@@ -487,7 +489,7 @@ def main():
                     help="time the per-row acceptance sums (sv_row_acceptance) on the same inputs instead of the "
                          "verify call, and print their own JSON line")
     ap.add_argument("--filtered", action="store_true",
-                    help="time the filtered verify (sampler filters on both sides) and its thresholds kernel")
+                    help="time the filtered verify (sampler filters on both sides) and its thresholds chain")
     ap.add_argument("--lazy", action="store_true",
                     help="time the lazy position-serial verify (sv_verify_batch_lazy) instead, and print its own "
                          "JSON line; its algorithmic bytes count only the rows it must read")

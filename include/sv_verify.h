@@ -436,7 +436,7 @@ void sv_get_tuning(sv_tuning* t);
  * a call whose shape changes the workspace layout, enqueue a small kernel
  * that zeroes the array's counters.
  */
-#define SV_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+#define SV_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
 
 sv_status sv_verify_batch_static(const void* target_logits, const void* draft_logits,
                                  const int32_t* draft_tokens, const int32_t* row_offsets,

@@ -277,7 +277,7 @@ def verify_batch(target, draft, draft_tokens, row_offsets, temperature, tau, see
     return out_tokens, out_accept_len
 
 
-STATIC_WORKSPACE_BYTES = 16 << 20  # SV_STATIC_WORKSPACE_BYTES
+STATIC_WORKSPACE_BYTES = 32 << 20  # SV_STATIC_WORKSPACE_BYTES
 
 
 def verify_batch_static(target, draft, draft_tokens, row_offsets, temperature, tau, seed: int, out_tokens,

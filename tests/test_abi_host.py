@@ -233,3 +233,4 @@ def test_static_entry_point_validates_on_the_host(lib):
     assert lib.sv_workspace_bytes(big) > STATIC_WORKSPACE_BYTES
     assert call(1024, 9216, 262144, 0) == WORKSPACE
     assert lib.sv_workspace_bytes(SvShape(512, 2560, 152064, 0)) <= STATIC_WORKSPACE_BYTES  # 512 x 5 x 152064 fits
+    assert lib.sv_workspace_bytes(SvShape(256, 2304, 256000, 1)) <= STATIC_WORKSPACE_BYTES  # 256 x 9 x 256000 fits

@@ -2885,28 +2885,29 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
     return i < ns ? (F.list[i] * SV + q % SV) * kWave + lane : nvec;
   };
   int nc = 0;
-  auto work = [&](int i0, int q0, int nq) __attribute__((always_inline)) {
+  uint32_t okbits = 0;  // bit q: this lane's vector q of the step lies inside the row
+  auto work = [&](int q0, int nq) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int q = 0; q < nq; ++q) {
       const CH x = F.stage[wave][q][lane];
-      const bool ok = vec_of(i0, q0 + q) < nvec;
-      float ts = 0.0f, vmax = -INFINITY;
-      int cnt = 0;
+      const bool ok = (okbits >> (q0 + q)) & 1u;
+      // The vector's largest and second largest logit: a lane holds two candidates or more
+      // iff the second reaches lo.
+      float a = -INFINITY, a2 = -INFINITY, ts = 0.0f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float v = x.get(e);
-        const bool cnd = ok && !(v < lo);
-        cnt += cnd ? 1 : 0;
-        vmax = cnd ? fmaxf(vmax, v) : vmax;
-        if (rest_on && ok && !cnd) ts += fast_exp2((v - m) * c);
+        a2 = __builtin_amdgcn_fmed3f(a, a2, v);
+        a = fmaxf(a, v);
+        if (rest_on && ok && v < lo) ts += fast_exp2((v - m) * c);
       }
       if (rest_on) tl += (double)ts;
-      const uint64_t any = __ballot(cnt > 0);
+      const uint64_t any = __ballot(ok && !(a < lo));
       if (any == 0) continue;  // the same for every lane
-      if (__ballot(cnt > 1) == 0) {
-        if (cnt > 0) {
+      if (__ballot(ok && !(a2 < lo)) == 0) {
+        if (ok && !(a < lo)) {
           const int pos = nc + lane_rank(any);
-          if (pos < kFinCap) cand[pos] = vmax;
+          if (pos < kFinCap) cand[pos] = a;
         }
         nc += (int)__popcll(any);
       } else {
@@ -2927,16 +2928,21 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   static_assert(kFinVecs == 2 * kFinStage, "two stage fills per step");
   for (int i0 = wave; i0 < ns; i0 += NS * kFinWaves) {
     CH x[kFinVecs];
+    okbits = 0;
 #pragma unroll
-    for (int q = 0; q < kFinVecs; ++q) x[q].load(row + (int64_t)min(vec_of(i0, q), nvec - 1) * VEC);
+    for (int q = 0; q < kFinVecs; ++q) {
+      const int vi = vec_of(i0, q);
+      okbits |= (uint32_t)(vi < nvec) << q;
+      x[q].load(row + (int64_t)min(vi, nvec - 1) * VEC);
+    }
     const int nv = min(NS, (ns - i0 + kFinWaves - 1) / kFinWaves) * SV;  // vectors of this step
 #pragma unroll
     for (int q = 0; q < kFinStage; ++q) F.stage[wave][q][lane] = x[q];  // each lane reads back its own
-    work(i0, 0, min(nv, kFinStage));
+    work(0, min(nv, kFinStage));
     if (nv > kFinStage) {
 #pragma unroll
       for (int q = 0; q < kFinStage; ++q) F.stage[wave][q][lane] = x[kFinStage + q];
-      work(i0, kFinStage, nv - kFinStage);
+      work(kFinStage, nv - kFinStage);
     }
   }
   const double tw = wave_sum(tl);

@@ -107,7 +107,8 @@ def _spec(V, dtype, B=24, spikes=True, seed=0, **kw):
 
 @pytest.mark.parametrize("V,dtype,spikes", [(37, "f32", True), (4096, "bf16", True), (4099, "bf16", True),
                                             (12289, "f32", False), (32000, "bf16", True), (32000, "bf16", False),
-                                            (70001, "f32", True)])
+                                            (70001, "f32", True), (8192, "f32", True), (20480, "bf16", False),
+                                            (512, "bf16", True)])
 def test_thresholds_match_oracle(V, dtype, spikes):
     batch = as_batch(wl.generate(_spec(V, dtype, spikes=spikes, seed=300 + V)))
     rng = np.random.default_rng(V)
@@ -139,6 +140,21 @@ def test_thresholds_exact_fallback_paths():
     b2["draft_filter"] = (np.array([1], np.int32), None, None)
     c2, _ = check_thresholds(b2, "all ties")
     assert c2 == 6
+
+
+def test_thresholds_moderately_flat_rows():
+    # Rows of 16384 logits at sigma 1.5: top-p alone keeps hundreds to thousands of tokens, so
+    # the records' candidates overflow and the exact path starts from the records' bound.
+    rng = np.random.default_rng(21)
+    V, B = 16384, 6
+    spec = wl.Spec(B=B, T=3, V=V, dtype="f32", sigma_t=1.5, sigma_d=1.0, temperature=(0.6, 1.2), rng_seed=5,
+                   verify_seed=1)
+    batch = as_batch(wl.generate(spec))
+    batch["target_filter"] = (None, rng.choice([0.3, 0.6, 0.9, 0.97], size=B).astype(np.float32), None)
+    batch["draft_filter"] = (rng.choice([0, 300, 700], size=B).astype(np.int32),
+                             rng.choice([1.0, 0.8], size=B).astype(np.float32), None)
+    checked, near = check_thresholds(batch, "moderately flat V=16384")
+    assert checked >= 40 and near <= 2
 
 
 def test_thresholds_invalid_rows_and_greedy():

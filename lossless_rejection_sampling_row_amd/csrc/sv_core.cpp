@@ -50,6 +50,8 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   off += (size_t)q.B * sizeof(int32_t);
   q.off_theta = off = align_up(off, 256);  // [R] (target, draft)
   off += (size_t)q.R * 2 * sizeof(float);
+  q.off_fstat = off = align_up(off, 256);  // [R] (target, draft)
+  off += (size_t)q.R * 2 * sizeof(FiltStat);
   q.off_ticket2 = off = align_up(off, 256);  // pass 2's request tickets
   off += (size_t)q.B * sizeof(uint32_t);
   q.off_bmax = off = align_up(off, 8);  // the bonus race's per-request best (logit, token)

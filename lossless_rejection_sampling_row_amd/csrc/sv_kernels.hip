@@ -57,9 +57,11 @@ struct FilterSide {
 struct FilterArgs {
   FilterSide side[2];  // target, draft
   float* theta;        // [R][2] keep-thresholds, written by thresholds_kernel
-  // With segment records (16-byte rows of at most kSegCap segments): the records, [R][2][nseg].
+  // With segment records (16-byte rows of at most kSegCap segments): the records, [R][2][nseg],
+  // and per row and side the statistics pass 1 can take instead of streaming the row.
   SegRec* seg = nullptr;
   int32_t nseg = 0;
+  FiltStat* fstat = nullptr;
 };
 
 struct Inputs {
@@ -79,6 +81,8 @@ struct Inputs {
   // parameters, whose validity pass 2 checks per request.
   const float* theta = nullptr;
   FilterSide filt[2] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
+  // With the filter chain's segment records: [R][2] statistics of the rows it decided.
+  const FiltStat* fstat = nullptr;
 };
 
 struct FilterParams {
@@ -485,9 +489,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     load_chunks<true>(da, drow, sp.begin, lane, sp.end);
   }
   float th_t = -INFINITY, th_d = -INFINITY;
+  FiltStat ft{}, fd{};
   if (FILT) {
     th_t = in.theta[2 * (int64_t)rg];
     th_d = in.theta[2 * (int64_t)rg + 1];
+    if (in.fstat != nullptr) {
+      ft = in.fstat[2 * (int64_t)rg];
+      fd = in.fstat[2 * (int64_t)rg + 1];
+    }
   }
   const RowCls cls = classify_slot(in, p, bg, lane);
   if (!cls.proposal) return;
@@ -495,6 +504,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   if (FILT && r != rg) {
     th_t = in.theta[2 * (int64_t)r];
     th_d = in.theta[2 * (int64_t)r + 1];
+    if (in.fstat != nullptr) {
+      ft = in.fstat[2 * (int64_t)r];
+      fd = in.fstat[2 * (int64_t)r + 1];
+    }
+  }
+  if (FILT && in.fstat != nullptr && ft.ok != 0 && fd.ok != 0) {
+    // The filter chain decided both sides from their candidates and kept the row's statistics:
+    // wave 0's partial carries them whole (and the drafted token's logits), the others none.
+    P1Part pp{};
+    if (g == 0) {
+      pp = P1Part{ft.m, ft.s, fd.m, fd.s, -1, -1, 2, ft.lD, fd.lD, {0, 0, 0}};
+    } else {
+      pp = P1Part{-INFINITY, 0.0f, -INFINITY, 0.0f, -1, -1, 0, 0.0f, 0.0f, {0, 0, 0}};
+    }
+    if (lane == 0) w.part1[(int64_t)r * in.w1 + g] = pp;
+    return;
   }
   if (r != rg) {  // the guess missed: stream the right row
     trow = reinterpret_cast<const E*>(in.target) + (int64_t)r * in.V;
@@ -2716,7 +2741,7 @@ struct FinSmem {
   double e[kFinCap];                                 // masses exp((x - m) / T), 0 below the base
   int cnt[kFinWaves];
   double rest[kFinWaves];
-  float th, lo, m;
+  float th, lo, m, s;
   int ns, mode, back;
 };
 
@@ -2751,8 +2776,20 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   const float T = in.temp[b];
   const FilterParams fp = filter_params(fa.side[side], b);
   const bool topk = fp.k > 0 && fp.k < in.V, topp = fp.top_p < 1.0f, minp = fp.min_p > 0.0f;
+  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
+  // The row's drafted token and its logit, for the statistics pass 1 may take from here: their
+  // loads are issued now and waited for at the end.
+  int Dv = -1;
+  float lD = 0.0f;
+  if (fa.fstat != nullptr && threadIdx.x == 0) {
+    Dv = in.dt[r];
+    if ((unsigned)Dv < (unsigned)in.V) lD = to_float(row[Dv]);
+  }
   auto done = [&](float th) __attribute__((always_inline)) {
-    if (threadIdx.x == 0) *out = th;
+    if (threadIdx.x == 0) {
+      *out = th;
+      if (fa.fstat != nullptr) fa.fstat[rs] = FiltStat{0.0f, 0.0f, 0.0f, 0};
+    }
   };
   if (!(T > 0.0f) || !temperature_ok(T) || !filter_valid(fp) || !(topk || topp || minp)) {
     done(-INFINITY);
@@ -2877,7 +2914,6 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // time, kFinVecs vectors per lane loaded at once and worked through the LDS stage
   // kFinStage at a time. A vector whose lanes hold at most one candidate each stores each
   // lane's largest logit at the lane's rank; otherwise one ballot per element.
-  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
   const int nvec = in.V / VEC;
   float* cand = F.cand[wave];
   auto vec_of = [&](int i0, int q) __attribute__((always_inline)) {
@@ -3019,6 +3055,14 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
       }
       th = fmaxf(fmaxf(th_k, th_p), th_m);
       back = 0;
+      // The masked sum pass 1 would take over the row: every kept logit is a candidate.
+      const float mc = ref_of(m, c);
+      float acc = 0.0f;
+      for (int j = lane; j < n; j += kWave) {
+        const float x = F.all[j];
+        if (!(x < th)) acc += fast_exp2(fmaf(x, c, -mc));
+      }
+      F.s = wave_sum(acc);
     } while (false);
     if (lane == 0) {
       F.th = th;
@@ -3027,12 +3071,17 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
   }
   __syncthreads();
   if (F.back == 0) {
-    done(F.th);
+    if (threadIdx.x == 0) {
+      *out = F.th;
+      if (fa.fstat != nullptr)
+        fa.fstat[rs] = FiltStat{m, F.s, lD, (unsigned)Dv < (unsigned)in.V ? 1 : 0};
+    }
     return;
   }
   if (rest_on) hint = lo;
   __syncthreads();  // the exact path reuses the LDS
   }
+  if (threadIdx.x == 0 && fa.fstat != nullptr) fa.fstat[rs] = FiltStat{0.0f, 0.0f, 0.0f, 0};
   thresholds_row<E, VEC>(in, fa, r, side, u.x, hint);
 }
 
@@ -3137,6 +3186,8 @@ hipError_t launch_thresholds(const Plan& p, const Inputs& in, FilterArgs fa, hip
   return hipGetLastError();
 }
 
+constexpr int kSentSpread = 4;  // pass-1 wave multiplier when the filter chain leaves row statistics
+
 template <typename E, int VEC, bool FILT = false>
 hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& out, hipStream_t stream,
                        hipEvent_t const* ev) {
@@ -3150,6 +3201,9 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   hipError_t err = resident_waves(k1, kTargetWavesPerCU, &slots1);
   if (err != hipSuccess) return err;
   if ((err = resident_waves(k2, kTargetWavesPerCU2, &slots2)) != hipSuccess) return err;
+  // When the filter chain leaves most rows' statistics, pass 1 streams only the rest: four
+  // times as many waves per row keeps their spans short.
+  if (FILT && in.fstat != nullptr) slots1 *= kSentSpread;
   const Launch l = pick_waves(p, slots1, slots2);
   in.w1 = l.w1;
   in.w2 = l.w2;
@@ -3277,7 +3331,13 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
     in.theta = reinterpret_cast<float*>(ws + p.off_theta);
     in.filt[0] = ft;
     in.filt[1] = fd;
-    const FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
+    FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
+    // With segment records the chain leaves the statistics of the rows it decided, and pass 1
+    // takes them instead of streaming those rows.
+    if (aligned && p.nseg > 0) {
+      fa.fstat = reinterpret_cast<FiltStat*>(ws + p.off_fstat);
+      in.fstat = fa.fstat;
+    }
     if (p.dtype == SV_BF16) {
       err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream, ws) : launch_thresholds<uint16_t, 1>(p, in, fa, stream, ws);
       if (err == hipSuccess)
@@ -3424,7 +3484,13 @@ static sv_status row_sums_run(const void* target_logits, const void* draft_logit
     in.theta = reinterpret_cast<float*>(ws + p.off_theta);
     in.filt[0] = ft;
     in.filt[1] = fd;
-    const FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
+    FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
+    // With segment records the chain leaves the statistics of the rows it decided, and pass 1
+    // takes them instead of streaming those rows.
+    if (aligned && p.nseg > 0) {
+      fa.fstat = reinterpret_cast<FiltStat*>(ws + p.off_fstat);
+      in.fstat = fa.fstat;
+    }
     if (p.dtype == SV_BF16) {
       err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream, ws) : launch_thresholds<uint16_t, 1>(p, in, fa, stream, ws);
       if (err == hipSuccess)

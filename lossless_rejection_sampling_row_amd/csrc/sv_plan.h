@@ -101,6 +101,15 @@ struct alignas(8) SegRec {
 };
 static_assert(sizeof(SegRec) == 8, "SegRec layout");
 
+// A row and side whose threshold the filter chain decided from its candidates (ok = 1): the
+// row's largest logit, the masked sum of exp2(l*c - ref_of(m, c)) over the kept logits, and
+// the logit at the row's drafted token. Pass 1 then writes the row's partials from it.
+struct FiltStat {
+  float m, s, lD;
+  int32_t ok;
+};
+static_assert(sizeof(FiltStat) == 16, "FiltStat layout");
+
 struct Plan {
   int32_t B, R, V, dtype;
   int32_t esize;  // bytes per logit
@@ -110,7 +119,7 @@ struct Plan {
   // Persistent: the header, lazy stop flags, keep-thresholds, then the counters every call
   // leaves at zero, [off_ticket2, off_trans). Per call, from off_trans: the partial records
   // (off_part1..3) or, earlier in the filter chain, the segment records (off_seg).
-  size_t off_hdr, off_lazy, off_theta, off_ticket2, off_bmax, off_done3, off_trans;
+  size_t off_hdr, off_lazy, off_theta, off_fstat, off_ticket2, off_bmax, off_done3, off_trans;
   size_t off_part1, off_part2, off_part3, off_seg, total;
 };
 

@@ -366,7 +366,10 @@ sv_status sv_filter_thresholds(const void* target_logits, const void* draft_logi
  * target_filter, draft_filter   host pointers to sv_filter, or NULL.
  * The call first computes every row's thresholds (sv_filter_thresholds, into
  * the workspace), then runs the two passes of sv_verify_batch with the masks.
- * Every other argument, the results and the errors are those of
+ * A row whose two sides the threshold step decided from the logits at or above
+ * a bound it keeps (the masked sums are then at hand) is not streamed again by
+ * the first pass; its sums differ from a streamed row's only in summation
+ * order. Every other argument, the results and the errors are those of
  * sv_verify_batch_sched. With both filters NULL it computes exactly what
  * sv_verify_batch_sched computes.
  */
@@ -386,8 +389,8 @@ sv_status sv_verify_batch_filtered(const void* target_logits, const void* draft_
  * q the filtered distributions of sv_filter (mlxcel PR #992, section What
  * changed), so that sum_x min(p, mu) is the row's acceptance probability under the
  * sampler's own configuration. A request whose filter values are invalid at
- * T > 0 gets NaN, as sv_verify_batch_filtered fails it. The call runs the
- * thresholds kernel first. target_filter, draft_filter: host pointers to
+ * T > 0 gets NaN, as sv_verify_batch_filtered fails it. The call computes the
+ * thresholds first. target_filter, draft_filter: host pointers to
  * sv_filter, or NULL. Every other argument, the results and the errors are
  * those of sv_row_acceptance; with both filters NULL it computes what
  * sv_row_acceptance computes.

@@ -39,10 +39,10 @@ sv_status make_plan(const sv_shape& s, Plan* p) {
   q.w1max = q.w2max = (int32_t)(w < 1 ? 1 : w > kMaxWavesPerRow ? kMaxWavesPerRow : w);
   if ((int64_t)q.R * q.w1max > INT32_MAX || (int64_t)q.B * q.w2max > INT32_MAX) return SV_E_UNSUPPORTED;
   // The persistent part first: the header, the lazy verify's per-request stop flags, the
-  // filtered verify's keep-thresholds and the counters that every call leaves at zero. Then
-  // the per-call part, which one call writes before it reads: the partial records of passes
-  // 1 and 2 and of the acceptance sums, or, earlier in a filtered call, the filter chain's
-  // segment records and fallback flags (the two sets are never live at once).
+  // filtered verify's keep-thresholds and row statistics, and the counters that every call
+  // leaves at zero. Then the per-call part, which one call writes before it reads: the partial
+  // records of passes 1 and 2 and of the acceptance sums, or, earlier in a filtered call, the
+  // filter chain's segment records (the two sets are never live at once).
   size_t off = 0;
   q.off_hdr = off;
   off += sizeof(WsHeader);

@@ -2613,17 +2613,15 @@ __global__ __launch_bounds__(kBlock) void match_emit_kernel(Inputs in, Work w, c
 
 // ====================================================================== filter chain: segment records
 
-// The filter chain's thresholds in three launches when rows are read in 16-byte vectors and
+// The filter chain's thresholds in two launches when rows are read in 16-byte vectors and
 // hold at most kSegCap segments (thresholds_kernel alone otherwise):
 //  - seg_records_kernel streams every row and side that has an active filter, nw waves each,
-//    and writes one SegRec per segment: what thresholds_kernel's pass A kept in LDS;
-//  - thresholds_finish_kernel takes one wave per row and side and decides the thresholds from
-//    the records as thresholds_kernel does after its pass A (the candidate bound, the gather
-//    of the listed segments, the sort, the top-p scan), with wave-level sorts and scans in
-//    LDS instead of workgroup barriers;
-//  - thresholds_kernel then runs only for the rows and sides the finish sent back: top-k
-//    beyond the segment count, more than kFinCap candidates, or a window that holds less
-//    than top_p of the mass (its exact fallbacks).
+//    and writes one SegRec per segment (its largest logit, and with top-p alone its mass);
+//  - thresholds_finish_kernel takes one workgroup per row and side and decides the thresholds
+//    from the records (the candidate bound, the gather of the listed segments, top-k and
+//    top-p over the candidates). The rows and sides the records cannot decide (top-k beyond
+//    the segment count, too many candidates, candidates short of top_p) take the exact path
+//    of thresholds_kernel (thresholds_row) in the same workgroup.
 
 // A record's segment holds kSegLogits logits, SV 16-byte vectors per lane of a wave (one of
 // bf16, two of fp32): lane l's v-th vector of segment sg is vector (sg * SV + v) * kWave + l

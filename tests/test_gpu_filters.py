@@ -379,6 +379,23 @@ def test_edge_case_rows():
         compare(b, gpu, ora)
 
 
+@pytest.mark.parametrize("V,dtype", [(262144, "bf16"), (300000, "bf16"), (262147, "f32")])
+def test_rows_at_and_beyond_the_segment_record_cap(V, dtype):
+    # 262144 logits make exactly the largest number of 512-logit segment records a row may
+    # have; 300000 aligned bf16 logits make more, and 262147 fp32 logits are not 16-byte
+    # aligned, so both take the single-kernel thresholds path. Thresholds and verify outputs
+    # must match the oracle on each.
+    batch = as_batch(wl.generate(_spec(V, dtype, B=6, seed=700 + V % 97)))
+    rng = np.random.default_rng(V % 1000)
+    B = len(batch["tau"])
+    batch["target_filter"] = random_filters(B, V, rng, ks=[0, 1, 20, 50, 5000])
+    batch["draft_filter"] = random_filters(B, V, rng, ks=[0, 1, 20, 50, 5000])
+    checked, near = check_thresholds(batch, f"V={V} {dtype}")
+    assert checked > 0 and near <= 0.02 * checked + 2
+    tot = _verify_parity(batch, range(2), f"V={V} {dtype}")
+    assert tot.flagged_requests <= 0.05 * tot.requests + 2
+
+
 def test_long_windows_read_thresholds_beyond_the_first_64_rows():
     # Requests of 80 and 70 rows, target equal to draft, so that every offered draft is accepted
     # and the walk goes past its first 64 rows (their thresholds are read from memory, not from

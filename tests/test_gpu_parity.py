@@ -68,6 +68,18 @@ def test_micro_batches(V, dtype):
     _parity(batch, seeds=range(12), label=f"micro V={V} {dtype}")
 
 
+@pytest.mark.parametrize("V,dtype", [(300001, "bf16"), (300001, "f32"), (524288, "bf16")])
+def test_long_rows(V, dtype):
+    # Rows longer than any workload's: 300001 logits are not 16-byte aligned in either dtype
+    # (the scalar path); 524288 aligned bf16 logits give pass 1 and pass 2 their largest
+    # per-row wave counts.
+    spec = wl.Spec(B=5, T=(1, 4), V=V, dtype=dtype, sigma_t=3.0, n_spikes=8, sigma_d=(0.5, 2.0),
+                   temperature=(0.6, 1.2), greedy_frac=0.2, tau=(0.0, 0.3), rng_seed=7100 + V % 89,
+                   verify_seed=V)
+    batch = as_batch(wl.generate(spec))
+    _parity(batch, seeds=range(3), label=f"long rows V={V} {dtype}")
+
+
 @pytest.mark.parametrize("cfg,seeds", [(2, (0, 1, 2)), (3, (0, 1, 2, 3))])
 def test_full_config(cfg, seeds):
     batch = as_batch(wl.config(cfg))

@@ -462,6 +462,62 @@ __device__ __forceinline__ void stream_span(const Inputs& in, const Work& w, int
   if (lane == 0) w.part1[(int64_t)r * in.w1 + g] = pp;  // read by pass 2, after this kernel
 }
 
+// The filtered verify's rows where the filter chain decided one side only: stream the other
+// side's array (side 0 target, 1 draft) as stream_span does, and take the decided side's
+// statistics from the chain (wave 0 carries them whole, the others none) and its drafted-token
+// logit from the same record. Rows with a chain record always hold a valid drafted token.
+template <typename E, int VEC, int U, bool FILT>
+__device__ __forceinline__ void stream_one(const Inputs& in, const Work& w, int r, int g, float T, int D,
+                                           const E* row, Span sp, Chunk<E, VEC> (&xa)[U], int lane, float th,
+                                           int side, const FiltStat& other) {
+  using CH = Chunk<E, VEC>;
+  constexpr int step = U * kWave;
+  CH xb[U];
+  const float c = fold_scale(T);
+  const int dvec = D / VEC;
+  const int de = D - dvec * VEC;
+  const bool holds_D = dvec >= sp.begin && dvec < sp.end;
+  Acc a = acc_empty();
+  int found = 0;
+  float lD = 0.0f;
+  auto fold1 = [&](const CH (&x)[U], int wb) __attribute__((always_inline)) {
+    const int vb = wb + lane;
+    fold_soft<true, FILT>(a, x, vb, c, th);
+    if (holds_D) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (vb + u * kWave == dvec) {
+          found = 1;
+          lD = x[u].get_dyn(de);
+        }
+      }
+    }
+  };
+  const int nsteps = (sp.end - sp.begin + step - 1) / step;
+  for (int i = 0, base = sp.begin; i < nsteps; i += 2, base += 2 * step) {
+    load_chunks<true>(xb, row, base + step, lane, sp.end);
+    mask_chunks(xa, base, lane, sp.end);
+    fold1(xa, base);
+    load_chunks<true>(xa, row, base + 2 * step, lane, sp.end);
+    mask_chunks(xb, base + step, lane, sp.end);
+    fold1(xb, base + step);
+  }
+  float m, sum;
+  int am;
+  wave_stat(a, c, true, m, sum, am);
+  const uint64_t fm = __ballot(found);
+  const float lDw = lane_of(lD, fm ? __ffsll((unsigned long long)fm) - 1 : 0);
+  const float om = g == 0 ? other.m : -INFINITY;
+  const float os = g == 0 ? other.s : 0.0f;
+  P1Part pp{};
+  if (side == 0) {
+    pp = P1Part{m, sum, om, os, am, -1, fm ? 2 : 0, lDw, other.lD, {0, 0, 0}};
+  } else {
+    pp = P1Part{om, os, m, sum, -1, -1, fm ? 2 : 0, other.lD, lDw, {0, 0, 0}};
+  }
+  if (lane == 0) w.part1[(int64_t)r * in.w1 + g] = pp;  // read by pass 2, after this kernel
+}
+
 template <typename E, int VEC, int U, bool FILT = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void pass1_kernel(Inputs in, Work w,
                                                                                              Outputs out) {
@@ -530,6 +586,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
   }
 
+  if (FILT && in.fstat != nullptr && (ft.ok != 0) != (fd.ok != 0)) {
+    if (ft.ok == 0)
+      stream_one<E, VEC, U, FILT>(in, w, r, g, cls.T, cls.D, trow, sp, ta, lane, th_t, 0, fd);
+    else
+      stream_one<E, VEC, U, FILT>(in, w, r, g, cls.T, cls.D, drow, sp, da, lane, th_d, 1, ft);
+    return;
+  }
   stream_span<E, VEC, U, FILT>(in, w, r, g, cls.T, cls.D, trow, drow, sp, ta, da, lane, th_t, th_d);
 }
 

@@ -61,11 +61,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def proposal_rows(w) -> int:
-    """Rows pass 1 streams: every row before a request's first no-proposal row and before its last row."""
+def proposal_rows(w, requests=None) -> int:
+    """Rows pass 1 streams: every row before a request's first no-proposal row and before its
+    last row (of the given requests, default all)."""
     ro, dt, V = w.row_offsets, w.draft_tokens, w.V
     n = 0
-    for b in range(w.B):
+    for b in (range(w.B) if requests is None else requests):
         lo, hi = int(ro[b]), int(ro[b + 1])
         for r in range(lo, hi - 1):
             if not (0 <= dt[r] < V):
@@ -323,20 +324,36 @@ def bench_lazy(args, binding, torch, sets, ws, stream):
     print(json.dumps(line), flush=True)
 
 
-def filtered_rows(w, filt) -> int:
-    """Rows the thresholds chain reads on one side: every row of a request with T > 0 and an
-    active filter on that side."""
+def filter_active(w, filt) -> np.ndarray:
+    """Per request: T > 0 and a filter that removes something."""
     k, tp, mp = filt
+    return (w.temperature > 0) & (((k > 0) & (k < w.V)) | (tp < 1.0) | (mp > 0.0))
+
+
+def filtered_rows(w, filt, draft_side=None) -> int:
+    """Rows the thresholds chain reads on one side: every row of a request with T > 0 and an
+    active filter on that side (sv_filter_thresholds). With draft_side set, only the rows the
+    verify reads on that side: a request's rows up to its first row without a proposal, less
+    that row on the draft side."""
     ro = w.row_offsets.astype(np.int64)
-    act = (w.temperature > 0) & (((k > 0) & (k < w.V)) | (tp < 1.0) | (mp > 0.0))
-    return int(np.sum(np.diff(ro)[act]))
+    act = filter_active(w, filt)
+    if draft_side is None:
+        return int(np.sum(np.diff(ro)[act]))
+    dt = w.draft_tokens
+    n = 0
+    for b in np.flatnonzero(act):
+        d = dt[ro[b]:ro[b + 1]]
+        f = int(np.flatnonzero((d < 0) | (d >= w.V))[0])  # the last row has none
+        n += f if draft_side else f + 1
+    return n
 
 
 def bench_filtered(args, binding, torch, sets, ws, stream):
     """K filtered verify calls (top-k / top-p / min-p on both sides), and K calls of the
     thresholds chain alone (sv_filter_thresholds: seg_records_kernel, then
     thresholds_finish_kernel). The chain's algorithmic bytes are one read of every row it
-    filters; the whole call adds pass 1's and pass 2's bytes."""
+    filters; the whole call's are one read of each filtered row side the verify reads, plus
+    pass 1's and pass 2's bytes."""
     from lossless_rejection_sampling_row_amd import workloads as wl
     K, W = args.steps, args.warmup
     nsets = len(sets)
@@ -385,10 +402,17 @@ def bench_filtered(args, binding, torch, sets, ws, stream):
     th_bytes = np.array([(filtered_rows(sets[i % nsets][0], filts[i % nsets][0][0])
                           + filtered_rows(sets[i % nsets][0], filts[i % nsets][0][1])) * V * esize
                          for i in range(K)], dtype=np.float64)
-    pair = np.array([proposal_rows(sets[i % nsets][0]) * V * 2 * esize + pass2_bytes(sets[i % nsets][0], lens[i], esize)
-                     for i in range(K)], dtype=np.float64)
+    # Pass 1 must read only the unfiltered sides of the proposal rows: the chain read the others.
+    def pair_bytes(i):
+        w, (tf, df) = sets[i % nsets][0], filts[i % nsets][0]
+        rows = sum(proposal_rows(w, np.flatnonzero(~filter_active(w, f))) for f in (tf, df))
+        return rows * V * esize + pass2_bytes(w, lens[i], esize)
+    pair = np.array([pair_bytes(i) for i in range(K)], dtype=np.float64)
+    used_bytes = np.array([(filtered_rows(sets[i % nsets][0], filts[i % nsets][0][0], draft_side=False)
+                            + filtered_rows(sets[i % nsets][0], filts[i % nsets][0][1], draft_side=True)) * V * esize
+                           for i in range(K)], dtype=np.float64)
     th_gbps = th_bytes.mean() / (ms_th / 1e3) / 1e9
-    gbps = (th_bytes.mean() + pair.mean()) / (ms / 1e3) / 1e9
+    gbps = (used_bytes.mean() + pair.mean()) / (ms / 1e3) / 1e9
     log(f"[bench] filtered verify: {ms * 1e3:.1f} us/step ({gbps:.0f} GB/s of algorithmic bytes); thresholds chain "
         f"alone {ms_th * 1e3:.1f} us ({th_gbps:.0f} GB/s, one read of each filtered row)")
     line = {
@@ -413,7 +437,7 @@ def bench_filtered(args, binding, torch, sets, ws, stream):
                      "kernel": "seg_records_kernel + thresholds_finish_kernel (one sv_filter_thresholds call)",
                      "launch_us": round(ms_th * 1e3, 2), "alg_bytes_per_launch": int(th_bytes.mean())},
         "whole_call": {"achieved": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                       "alg_bytes_per_call": int(th_bytes.mean() + pair.mean())},
+                       "alg_bytes_per_call": int(used_bytes.mean() + pair.mean())},
     }
     print(json.dumps(line), flush=True)
 

@@ -62,6 +62,8 @@ struct FilterArgs {
   SegRec* seg = nullptr;
   int32_t nseg = 0;
   FiltStat* fstat = nullptr;
+  // Filtered verify only: skip the row sides the verify never reads (side_unused).
+  int32_t skip_unused = 0;
 };
 
 struct Inputs {
@@ -2676,6 +2678,20 @@ __global__ __launch_bounds__(kBlock) void match_emit_kernel(Inputs in, Work w, c
 
 // ====================================================================== filter chain: segment records
 
+// Row sides whose keep-threshold the verify never reads. A request stops at its first row
+// without a proposal (a drafted token outside [0, V); every request's last row is one), and
+// that row draws from p alone. So the draft side of such a row is never read, nor either side
+// of the rows after it. Row r of request b; wave-uniform.
+__device__ __forceinline__ bool side_unused(const Inputs& in, int b, int r, int side, int lane) {
+  const int lo = min(max(in.ro[b], 0), r);
+  for (int base = lo; base < r; base += kWave) {
+    const int j = base + lane;
+    const bool none = j < r && (unsigned)in.dt[j] >= (unsigned)in.V;
+    if (__ballot(none) != 0) return true;
+  }
+  return side == 1 && (unsigned)in.dt[r] >= (unsigned)in.V;
+}
+
 // The filter chain's thresholds in two launches when rows are read in 16-byte vectors and
 // hold at most kSegCap segments (thresholds_kernel alone otherwise):
 //  - seg_records_kernel streams every row and side that has an active filter, nw waves each,
@@ -2705,13 +2721,19 @@ __global__ __launch_bounds__(kBlock) void seg_records_kernel(Inputs in, FilterAr
   const FilterParams fp = filter_params(fa.side[side], b);
   const bool topk = fp.k > 0 && fp.k < in.V, topp = fp.top_p < 1.0f, minp = fp.min_p > 0.0f;
   if (!(T > 0.0f) || !temperature_ok(T) || !filter_valid(fp) || !(topk || topp || minp)) return;
-  const bool mass = topp && !topk;
-  const float c = scale_of(T);
   const int nseg = fa.nseg, nvec = in.V / VEC;
   const int per = (nseg + nw - 1) / nw;
   const int s0 = min(g * per, nseg), s1 = min(s0 + per, nseg);
-  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
   SegRec* rec = fa.seg + (int64_t)rs * nseg;
+  if (fa.skip_unused && side_unused(in, b, r, side, lane)) {
+    // Not streamed: each wave marks its first record (a negative mass, which no sum of
+    // exponentials gives), and the finishing kernel writes -inf for the side.
+    if (lane == 0 && s0 < s1) rec[s0] = SegRec{-INFINITY, -1.0f};
+    return;
+  }
+  const bool mass = topp && !topk;
+  const float c = scale_of(T);
+  const E* row = reinterpret_cast<const E*>(side == 0 ? in.target : in.draft) + (int64_t)r * in.V;
   using CH = Chunk<E, VEC>;
   constexpr int U = 2 / SV;  // segments per step (two vectors per lane), two steps in flight
   auto vec_of = [&](int sg, int v) __attribute__((always_inline)) { return (sg * SV + v) * kWave + lane; };
@@ -2870,7 +2892,7 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
     const SegRec* rec = fa.seg + (int64_t)rs * nseg;
     float smax[RS], smass[RS];
     float mx = -INFINITY;
-    int bad = 0;
+    int bad = 0, unread = 0;
 #pragma unroll
     for (int t = 0; t < RS; ++t) {
       smax[t] = -INFINITY;
@@ -2881,12 +2903,16 @@ __global__ __launch_bounds__(kFiltBlock) __attribute__((amdgpu_waves_per_eu(6)))
         smass[t] = q.mass;
       }
       bad |= (int)!(smax[t] < INFINITY);
+      unread |= (int)(smass[t] < 0.0f);
       mx = fmaxf(mx, smax[t]);
     }
     const float m = wave_max(mx);
     int mode = 1, ns = 0;
     float th = 0.0f, lo = 0.0f;
-    if (wave_or(bad) != 0 || m == -INFINITY) {
+    if (fa.skip_unused && wave_or(unread) != 0) {
+      mode = 0;  // a side the verify never reads, which the record kernel did not stream
+      th = -INFINITY;
+    } else if (wave_or(bad) != 0 || m == -INFINITY) {
       mode = 0;
       th = INFINITY;
     } else {
@@ -3394,10 +3420,12 @@ static sv_status run(const void* target, const void* draft, const int32_t* draft
     in.filt[1] = fd;
     FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
     // With segment records the chain leaves the statistics of the rows it decided, and pass 1
-    // takes them instead of streaming those rows.
+    // takes them instead of streaming those rows; the chain skips the row sides the verify
+    // never reads.
     if (aligned && p.nseg > 0) {
       fa.fstat = reinterpret_cast<FiltStat*>(ws + p.off_fstat);
       in.fstat = fa.fstat;
+      fa.skip_unused = 1;
     }
     if (p.dtype == SV_BF16) {
       err = aligned ? launch_thresholds<uint16_t, 8>(p, in, fa, stream, ws) : launch_thresholds<uint16_t, 1>(p, in, fa, stream, ws);

@@ -364,12 +364,14 @@ sv_status sv_filter_thresholds(const void* target_logits, const void* draft_logi
  * an accepted draft has p(D) > 0, and both draws put no mass outside p's
  * support.
  * target_filter, draft_filter   host pointers to sv_filter, or NULL.
- * The call first computes every row's thresholds (sv_filter_thresholds, into
+ * The call first computes the rows' thresholds (as sv_filter_thresholds, into
  * the workspace), then runs the two passes of sv_verify_batch with the masks.
- * A row whose two sides the threshold step decided from the logits at or above
- * a bound it keeps (the masked sums are then at hand) is not streamed again by
- * the first pass; its sums differ from a streamed row's only in summation
- * order. Every other argument, the results and the errors are those of
+ * It skips the row sides the method never reads: the draft side of a row with
+ * no proposal (every request's last row is one) and both sides of the rows
+ * after it. A row side that the threshold step decided from the logits at or
+ * above a bound it keeps (the masked sums are then at hand) is not streamed
+ * again by the first pass; its sums differ from a streamed side's only in
+ * summation order. Every other argument, the results and the errors are those of
  * sv_verify_batch_sched. With both filters NULL it computes exactly what
  * sv_verify_batch_sched computes.
  */

@@ -392,7 +392,8 @@ sv_status sv_verify_batch_filtered(const void* target_logits, const void* draft_
  * changed), so that sum_x min(p, mu) is the row's acceptance probability under the
  * sampler's own configuration. A request whose filter values are invalid at
  * T > 0 gets NaN, as sv_verify_batch_filtered fails it. The call computes the
- * thresholds first. target_filter, draft_filter: host pointers to
+ * thresholds first, skipping the row sides sv_verify_batch_filtered skips (no
+ * proposal row's sum reads them). target_filter, draft_filter: host pointers to
  * sv_filter, or NULL. Every other argument, the results and the errors are
  * those of sv_row_acceptance; with both filters NULL it computes what
  * sv_row_acceptance computes.

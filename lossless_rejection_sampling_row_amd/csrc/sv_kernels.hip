@@ -3575,8 +3575,10 @@ static sv_status row_sums_run(const void* target_logits, const void* draft_logit
     in.filt[1] = fd;
     FilterArgs fa{{ft, fd}, reinterpret_cast<float*>(ws + p.off_theta)};
     // With segment records the chain leaves the statistics of the rows it decided, and pass 1
-    // takes them instead of streaming those rows.
+    // takes them instead of streaming those rows. The sums read only proposal rows, so the
+    // chain skips the row sides the verify never reads here too.
     if (aligned && p.nseg > 0) {
+      fa.skip_unused = 1;
       fa.fstat = reinterpret_cast<FiltStat*>(ws + p.off_fstat);
       in.fstat = fa.fstat;
     }

@@ -3274,6 +3274,7 @@ hipError_t launch_thresholds(const Plan& p, const Inputs& in, FilterArgs fa, hip
 }
 
 constexpr int kSentSpread = 4;  // pass-1 wave multiplier when the filter chain leaves row statistics
+constexpr int kSentWaves = 16;  // and the fewest pass-1 waves per row then
 
 template <typename E, int VEC, bool FILT = false>
 hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& out, hipStream_t stream,
@@ -3291,7 +3292,18 @@ hipError_t launch_pair(const Plan& p, Inputs in, const Work& w, const Outputs& o
   // When the filter chain leaves most rows' statistics, pass 1 streams only the rest: four
   // times as many waves per row keeps their spans short.
   if (FILT && in.fstat != nullptr) slots1 *= kSentSpread;
-  const Launch l = pick_waves(p, slots1, slots2);
+  Launch l = pick_waves(p, slots1, slots2);
+  // A batch of many rows would still give each row few waves, and the waves of the rows left
+  // to stream would then take long spans: keep at least kSentWaves per row (unless a tuning
+  // override sets the split).
+  if (FILT && in.fstat != nullptr && tuning().w1 <= 0 && l.w1 < kSentWaves) {
+    int w1 = l.w1;
+    while (w1 * 2 <= kSentWaves && w1 * 2 <= p.w1max) w1 *= 2;
+    const int64_t rows = p.R - p.B;
+    l.w1 = w1;
+    l.blocks1 = (rows * w1 + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (l.blocks1 < 1) l.blocks1 = 1;
+  }
   in.w1 = l.w1;
   in.w2 = l.w2;
   if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
